@@ -1,0 +1,258 @@
+/*
+ * pkv.h -- C ABI of the paged KV-cache attention library for AMD MI355X (gfx950).
+ *
+ * The library appends new K/V rows into a paged cache addressed through a page
+ * table, and runs grouped-query attention over that cache for decode (one new
+ * query token per batch row) and for packed variable-length prefill (causal,
+ * optionally sliding-window, each sequence seeing only its own slot).  Every
+ * step runs in hand-written HIP kernels for gfx950.
+ *
+ * Pages cited below (a section is a file shown on that page):
+ *   [moe-qwen3 compare]
+ *     https://git.jhoeven.net/ceos/unsloth/compare/main...danielhanchen/flex-moe-qwen3
+ *   [continuous-batching compare]
+ *     https://git.jhoeven.net/ceos/unsloth/compare/main...transformers-continuous-batching-qwen3
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - bf16 tensors are passed as `void*` to 16-bit storage (IEEE bfloat16).
+ * - "device" pointers must be device memory of the current HIP device (or
+ *   memory the device can read/write); "host" pointers are plain host memory.
+ * - Ownership: the caller owns every buffer.  Compute entry points never
+ *   allocate, free or synchronise, and keep no device state between calls.
+ *   They only enqueue kernels on `stream` (a hipStream_t; NULL = the null
+ *   stream) and return; results are ready when the stream reaches them.
+ * - Errors: arguments are checked on the host before anything is enqueued;
+ *   on a bad argument the call returns a non-zero pkv_status, enqueues nothing
+ *   and leaves a message for pkv_last_error().  Device-side contents (page ids,
+ *   lengths, slots) cannot be checked on the host; the kernels bounds-check
+ *   them instead and never read or write outside the buffers described here:
+ *   a page id outside [1, n_pages), a slot outside [1, max_slots) or a
+ *   position beyond pages_per_slot*page_size is skipped (append) or treated
+ *   as an idle row / absent key (attention).  Such inputs are caller errors
+ *   and their results are unspecified, but never out of bounds.
+ *
+ * Cache layout (one K pool and one V pool per layer, same page geometry):
+ *   K pool: bf16 [n_pages][n_kv_heads][page_size][head_dim]   (token rows)
+ *   V pool: bf16 [n_pages][n_kv_heads][head_dim][page_size]   (d-major rows)
+ *   The pages' cache is a single (1, H, n_pages*page_size, D) buffer per K/V
+ *   ([continuous-batching compare] flex_paged_attention.py, PagedKVCache);
+ *   here pages are the outer dimension so one (page, head) block is contiguous,
+ *   and V is stored d-major inside a page so the P.V contraction can feed the
+ *   matrix cores straight from memory.
+ *
+ * Page table ([continuous-batching compare] flex_paged_attention.py, PageTable):
+ *   int32 [max_slots][pages_per_slot], entry = physical page of
+ *   (slot, logical page), -1 = unmapped.  Token at logical position `pos` of
+ *   `slot` lives in page table[slot][pos / page_size], row pos % page_size.
+ *   Slot 0 is the reserved no-op slot: it is never read or written.  Page 0
+ *   is reserved and never handed out by the allocator below.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,  /* null pointer, bad size, inconsistent shapes       */
+  PKV_ERR_UNSUPPORTED = 2,  /* head_dim / page_size / GQA ratio not implemented    */
+  PKV_ERR_LAUNCH = 3,       /* a kernel launch failed (HIP error text attached)   */
+  PKV_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required         */
+  PKV_ERR_CAPACITY = 5      /* allocator: no free slot / not enough free pages     */
+} pkv_status;
+
+/* One layer's pools.  Supported: head_dim in {64, 128, 256, 512};
+ * page_size a power of two in [16, 256]; n_pages >= 2. */
+typedef struct {
+  int32_t n_pages;     /* physical pages, including reserved page 0 */
+  int32_t page_size;   /* tokens per page                            */
+  int32_t n_kv_heads;
+  int32_t head_dim;
+} pkv_cache_desc;
+
+/* Device page table (see layout above). */
+typedef struct {
+  const int32_t* table;   /* device, int32 [max_slots][pages_per_slot]        */
+  int32_t max_slots;      /* usable slots + 1 (slot 0 reserved)               */
+  int32_t pages_per_slot; /* row stride, in entries                           */
+} pkv_page_table;
+
+/* Fused Qwen3 prologue for prefill: per token and head,
+ *   x <- RMSNorm(x) * w  over head_dim  (fp32: x / sqrt(mean(x^2) + eps) * w)
+ *   x <- x * cos + rotate_half(x) * sin, rotate_half(x) = (-x[D/2:], x[:D/2])
+ * applied to q (in place) and k; the new k and the raw v are appended to the
+ * pages.  Order and formulas: [moe-qwen3 compare]
+ * unsloth/inference/flex_gemma4_moe.py, attention forward (q_norm / k_norm,
+ * then rotary, then the paged-KV write) and _rotate_half / _apply_rotary_full.
+ * The cos/sin tables are fp32 [max_pos][head_dim/2] (see pkv_rope_table); a
+ * token at position p uses row p.  Positions >= max_pos are an error on the
+ * device side: the token is skipped (not appended, q left raw). */
+typedef struct {
+  const void* q_norm_w;   /* device bf16 [head_dim]                     */
+  const void* k_norm_w;   /* device bf16 [head_dim]                     */
+  float eps;              /* RMSNorm epsilon (Qwen3: 1e-6)              */
+  const float* rope_cos;  /* device fp32 [max_pos][head_dim/2]          */
+  const float* rope_sin;  /* device fp32 [max_pos][head_dim/2]          */
+  int32_t max_pos;
+  const void* k_raw;      /* device bf16 [total_tokens][n_kv][head_dim] */
+  const void* v_raw;      /* device bf16 [total_tokens][n_kv][head_dim] */
+} pkv_prologue;
+
+/* ---------------------------------------------------------------------------
+ * pkv_append -- scatter T new K/V rows into the pools (bit copy).
+ * [continuous-batching compare] flex_paged_attention.py, PageTable.assign
+ * (decode form, one token per batch row) and assign_prefill_no_paging (packed
+ * prefill form): token t goes to page table[slot[t]][pos[t] / page_size], row
+ * pos[t] % page_size, of kv head h, for every h.
+ *   k_new, v_new : device bf16 [T][n_kv_heads][head_dim]
+ *   slot, pos    : device int32 [T]; slot 0 = no-op token (skipped)
+ *   k_pool/v_pool: device bf16 pools (layout above), written in place
+ * Two tokens with the same (slot, pos) in one call: unspecified which wins.
+ * T == 0 is a no-op.
+ */
+pkv_status pkv_append(const void* k_new, const void* v_new, const int32_t* slot,
+                      const int32_t* pos, int32_t T, pkv_page_table pt,
+                      const pkv_cache_desc* cd, void* k_pool, void* v_pool, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pkv_attn_decode -- one query token per batch row against its slot's pages.
+ * Masks: the query sits at position L-1 (L = seq_lens[b], the key count after
+ * the append) and sees key j iff j <= L-1 and, with window W > 0, L-1-j < W
+ * ([continuous-batching compare] flex_paged_attention.py,
+ * create_causal_blockmask; [moe-qwen3 compare] flex_gemma4_moe.py,
+ * _decode_block_mask and _create_sliding_causal_blockmask).  GQA: query head
+ * h reads kv head h / (n_q_heads / n_kv_heads).
+ *   q        : device bf16 [B][n_q_heads][head_dim]
+ *   slots    : device int32 [B]; seq_lens: device int32 [B]
+ *              rows with slot 0 or seq_len 0 are idle: out = 0, lse = -inf,
+ *              nothing read ([continuous-batching compare] results write-up:
+ *              padded rows must come out as zeros, not NaN)
+ *   max_seq_len_hint : host int >= 1, an upper bound of seq_lens used to size
+ *              the split-K grid (results stay correct if exceeded; only speed
+ *              changes)
+ *   scale    : softmax scale applied to q.k (e.g. 1/sqrt(head_dim))
+ *   window   : 0 = full causal, W > 0 = sliding window of W keys incl. self
+ *   out      : device bf16 [B][n_q_heads][head_dim]
+ *   lse      : device fp32 [B][n_q_heads] natural-log sum-exp, or NULL
+ *   workspace: device scratch of >= pkv_decode_workspace_size(...) bytes
+ *              (NULL allowed when that size is 0); contents need no init.
+ * n_q_heads / n_kv_heads must be an integer G in [1, 16] with G * head_dim <= 2048
+ * (PKV_ERR_UNSUPPORTED otherwise).  B == 0 is a no-op.
+ */
+pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slots,
+                           const int32_t* seq_lens, int32_t B, int32_t max_seq_len_hint,
+                           pkv_page_table pt, const pkv_cache_desc* cd,
+                           const void* k_pool, const void* v_pool, float scale,
+                           int32_t window, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pkv_attn_decode needs for these sizes (0 = none). */
+size_t pkv_decode_workspace_size(int32_t B, int32_t n_q_heads, int32_t n_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len_hint,
+                                 int32_t window);
+
+/* ---------------------------------------------------------------------------
+ * pkv_attn_prefill -- packed varlen prefill, K/V read from the pages.
+ * Sequence n owns packed tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 of slot
+ * slots[n]; its query i sits at position start_pos[n] + i and sees keys
+ * 0 .. start_pos[n]+i of its own slot (document-causal mask,
+ * [continuous-batching compare] flex_paged_attention.py,
+ * create_prefill_blockmask_no_paging; sliding form [moe-qwen3 compare]
+ * flex_gemma4_moe.py, _create_prefill_sliding_blockmask).  Packing follows the
+ * engine's _prefill (prompts concatenated, positions restart at 0 per prompt).
+ * With `pro` == NULL every key must already be in the pages (e.g. through
+ * pkv_append); with `pro` != NULL the prologue first normalises and rotates q
+ * in place and k, and appends k and the raw v at the queries' positions.
+ *   q          : device bf16 [total_tokens][n_q_heads][head_dim]
+ *                (rewritten in place when pro != NULL)
+ *   cu_seqlens : device int32 [n_seqs+1], non-decreasing, cu[0] = 0,
+ *                cu[n_seqs] = total_tokens
+ *   slots      : device int32 [n_seqs]; slot 0 = padding sequence: its rows
+ *                get out = 0 / lse = -inf, nothing appended or read
+ *   start_pos  : device int32 [n_seqs] (cached prefix length) or NULL = all 0
+ *   max_seqlen_q_hint : host int >= 1, bound of the per-sequence token counts
+ *                used for grid sizing (correct if exceeded; only speed changes)
+ *   out        : device bf16 [total_tokens][n_q_heads][head_dim]
+ *   lse        : device fp32 [total_tokens][n_q_heads] or NULL
+ *   workspace  : unused by the current kernels (pass NULL / 0)
+ * head_dim 512 is not supported here (PKV_ERR_UNSUPPORTED).
+ */
+pkv_status pkv_attn_prefill(void* q, int32_t n_q_heads, const int32_t* cu_seqlens,
+                            const int32_t* slots, const int32_t* start_pos,
+                            int32_t n_seqs, int32_t total_tokens,
+                            int32_t max_seqlen_q_hint, pkv_page_table pt,
+                            const pkv_cache_desc* cd, void* k_pool, void* v_pool,
+                            float scale, int32_t window, const pkv_prologue* pro,
+                            void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pkv_rope_table -- fill fp32 cos/sin tables [max_pos][head_dim/2] with
+ * cos(p * theta^(-2i/head_dim)), sin(...), computed in fp64 on the device and
+ * rounded to fp32.  This is the "default" rope frequency set (the rope type
+ * the pages name for Qwen3-style layers, [moe-qwen3 compare]
+ * flex_gemma4_moe.py module docstring); the cos/sin are computed once and
+ * reused by every layer, as the engine computes them once per step.
+ *   cos_out, sin_out : device fp32 [max_pos][head_dim/2]
+ */
+pkv_status pkv_rope_table(float* cos_out, float* sin_out, int32_t max_pos,
+                          int32_t head_dim, double theta, void* stream);
+
+/* Thread-local text of the last non-OK status returned on this thread. */
+const char* pkv_last_error(void);
+
+/* Library version string, e.g. "pkv 0.1.0 gfx950". */
+const char* pkv_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Host-side slot / page allocator ([continuous-batching compare]
+ * flex_paged_attention.py, PageTable: can_reserve, allocate, reserve, erase).
+ * Pure host code; it owns only its own host memory and never touches a device.
+ * - free pages start as n_pages-1, ..., 2, 1 used as a stack (page 0 never
+ *   granted); free slots likewise max_slots-1 ... 1 (slot 0 never granted),
+ *   so slots come out 1, 2, 3, ...
+ * - reserve(slot, seq_len) grows the slot's capacity (tokens, a multiple of
+ *   page_size) to >= seq_len by granting the last k free pages, in stack
+ *   order, as its next logical pages; dry_run only reports whether it fits;
+ *   otherwise running out is PKV_ERR_CAPACITY with nothing changed.
+ * - erase(slot) frees the slot and pushes its pages back in reverse order;
+ *   its exported row stays as it was until the slot is allocated again
+ *   (allocate resets it to -1), as the pages' device table does.
+ * - export renders the device-format table [max_slots][pages_per_slot]
+ *   (row 0 all 0, unmapped -1) into a host buffer; the caller copies it to
+ *   the device.
+ */
+typedef struct pkv_pt pkv_pt;
+
+pkv_status pkv_pt_create(int32_t n_pages, int32_t page_size, int32_t max_slots,
+                         pkv_pt** out);
+void pkv_pt_destroy(pkv_pt* pt);
+int32_t pkv_pt_pages_available(const pkv_pt* pt);
+int32_t pkv_pt_free_slot_count(const pkv_pt* pt);
+/* slot < 0: may a NEW request of `size` tokens be admitted (enough free pages
+ * and a free slot)?  slot >= 1: dry-run reserve of that slot to `size`. */
+pkv_status pkv_pt_can_reserve(const pkv_pt* pt, int32_t size, int32_t slot, int32_t* ok);
+pkv_status pkv_pt_allocate(pkv_pt* pt, int32_t* slot_out);
+pkv_status pkv_pt_reserve(pkv_pt* pt, int32_t slot, int32_t seq_len, int32_t dry_run,
+                          int32_t* ok_out);
+pkv_status pkv_pt_erase(pkv_pt* pt, int32_t slot);
+int32_t pkv_pt_capacity(const pkv_pt* pt, int32_t slot);
+/* Copies up to max_out page ids owned by `slot` (logical order); returns the
+ * count owned (may exceed max_out), or -1 for a bad slot. */
+int32_t pkv_pt_row(const pkv_pt* pt, int32_t slot, int32_t* pages_out, int32_t max_out);
+/* Copies up to max_out entries of the free-page stack (bottom first); returns
+ * its full length. */
+int32_t pkv_pt_free_pages(const pkv_pt* pt, int32_t* pages_out, int32_t max_out);
+pkv_status pkv_pt_export(const pkv_pt* pt, int32_t* table_out, int32_t pages_per_slot);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,254 @@
+"""Paged KV-cache attention for AMD MI355X (gfx950): Python binding.
+
+Thin argument marshalling over the C ABI in ``include/pkv.h``; every step of
+the computation runs in the HIP kernels of ``libpkv.so``.  torch provides
+device memory and streams only.  There is no CPU fallback: if the library is
+not built, every call raises.
+
+Tensors (all on the same HIP device, contiguous):
+
+* ``k_pool``: bf16 ``[n_pages, n_kv, page_size, head_dim]``
+* ``v_pool``: bf16 ``[n_pages, n_kv, head_dim, page_size]`` (d-major pages)
+* ``table``:  int32 ``[max_slots, pages_per_slot]``, -1 = unmapped, slot 0
+  reserved
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import CacheDesc, PageTableRef, Prologue, PkvError, check, lib
+
+__all__ = ["append", "attn_decode", "attn_prefill", "decode_workspace_size", "rope_table",
+           "new_pools", "PageAllocator", "PkvError", "lib"]
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _bits16(t, name):
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold bf16 (bfloat16 / 16-bit view), got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _i32(t, name):
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 tensor")
+    return t
+
+
+def _cache(k_pool, v_pool, table):
+    _bits16(k_pool, "k_pool")
+    _bits16(v_pool, "v_pool")
+    _i32(table, "table")
+    if k_pool.dim() != 4 or v_pool.dim() != 4:
+        raise ValueError("pools must be 4-D")
+    n_pages, n_kv, ps, D = k_pool.shape
+    if tuple(v_pool.shape) != (n_pages, n_kv, D, ps):
+        raise ValueError(f"v_pool must be [n_pages, n_kv, head_dim, page_size] = "
+                         f"{(n_pages, n_kv, D, ps)}, got {tuple(v_pool.shape)}")
+    if table.dim() != 2:
+        raise ValueError("table must be [max_slots, pages_per_slot]")
+    cd = CacheDesc(n_pages, ps, n_kv, D)
+    pt = PageTableRef(table.data_ptr(), table.shape[0], table.shape[1])
+    return cd, pt
+
+
+def new_pools(n_pages, n_kv, page_size, head_dim, device="cuda", fill=None):
+    """Allocate a K and a V pool (bf16) in the library's layout."""
+    k = torch.empty((n_pages, n_kv, page_size, head_dim), dtype=torch.bfloat16, device=device)
+    v = torch.empty((n_pages, n_kv, head_dim, page_size), dtype=torch.bfloat16, device=device)
+    if fill is not None:
+        k.view(torch.int16).fill_(fill)
+        v.view(torch.int16).fill_(fill)
+    return k, v
+
+
+def append(k_new, v_new, slot, pos, table, k_pool, v_pool, stream=None):
+    """Scatter ``k_new/v_new [T, n_kv, D]`` to (slot, pos) of the pools."""
+    cd, pt = _cache(k_pool, v_pool, table)
+    _bits16(k_new, "k_new")
+    _bits16(v_new, "v_new")
+    _i32(slot, "slot")
+    _i32(pos, "pos")
+    T = k_new.shape[0]
+    if tuple(k_new.shape) != (T, cd.n_kv_heads, cd.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must be [T, n_kv, head_dim]")
+    if slot.numel() != T or pos.numel() != T:
+        raise ValueError("slot / pos must have T entries")
+    check(lib().pkv_append(_ptr(k_new), _ptr(v_new), _ptr(slot), _ptr(pos), T, pt,
+                           ctypes.byref(cd), _ptr(k_pool), _ptr(v_pool),
+                           _stream(stream, k_pool.device)))
+
+
+def decode_workspace_size(B, n_q, n_kv, head_dim, max_seq_len_hint, window=0):
+    return int(lib().pkv_decode_workspace_size(B, n_q, n_kv, head_dim, max_seq_len_hint,
+                                               window))
+
+
+def attn_decode(q, slots, seq_lens, table, k_pool, v_pool, scale=None, window=0,
+                max_seq_len_hint=None, out=None, lse=None, workspace=None, stream=None):
+    """Decode attention; returns ``out [B, n_q, D]`` (bf16)."""
+    cd, pt = _cache(k_pool, v_pool, table)
+    _bits16(q, "q")
+    _i32(slots, "slots")
+    _i32(seq_lens, "seq_lens")
+    B, n_q, D = q.shape
+    if D != cd.head_dim:
+        raise ValueError("q head_dim does not match the pools")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_seq_len_hint is None:
+        max_seq_len_hint = pt.pages_per_slot * cd.page_size
+    if out is None:
+        out = torch.empty((B, n_q, D), dtype=torch.bfloat16, device=q.device)
+    ws_bytes = decode_workspace_size(B, n_q, cd.n_kv_heads, D, max_seq_len_hint, window)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    wsize = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().pkv_attn_decode(_ptr(q), n_q, _ptr(slots), _ptr(seq_lens), B,
+                                int(max_seq_len_hint), pt, ctypes.byref(cd), _ptr(k_pool),
+                                _ptr(v_pool), float(scale), int(window), _ptr(out), _ptr(lse),
+                                _ptr(workspace), wsize, _stream(stream, q.device)))
+    return out
+
+
+def rope_table(max_pos, head_dim, theta, device="cuda", stream=None):
+    """fp32 ``cos, sin [max_pos, head_dim/2]`` of the default rope frequencies."""
+    c = torch.empty((max_pos, head_dim // 2), dtype=torch.float32, device=device)
+    s = torch.empty_like(c)
+    check(lib().pkv_rope_table(_ptr(c), _ptr(s), max_pos, head_dim, float(theta),
+                               _stream(stream, c.device)))
+    return c, s
+
+
+def attn_prefill(q, cu_seqlens, slots, table, k_pool, v_pool, scale=None, window=0,
+                 start_pos=None, max_seqlen_q_hint=None, prologue=None, out=None, lse=None,
+                 stream=None):
+    """Packed varlen prefill attention; returns ``out [T, n_q, D]`` (bf16).
+
+    ``prologue`` (optional) is a dict with ``q_norm_w, k_norm_w, eps, cos, sin,
+    k, v``: q is then normalised and rotated in place and k (normalised and
+    rotated) and v are appended before the attention.
+    """
+    cd, pt = _cache(k_pool, v_pool, table)
+    _bits16(q, "q")
+    _i32(cu_seqlens, "cu_seqlens")
+    _i32(slots, "slots")
+    if start_pos is not None:
+        _i32(start_pos, "start_pos")
+    T, n_q, D = q.shape
+    n_seqs = slots.numel()
+    if cu_seqlens.numel() != n_seqs + 1:
+        raise ValueError("cu_seqlens must have n_seqs + 1 entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_seqlen_q_hint is None:
+        max_seqlen_q_hint = max(T, 1)
+    if out is None:
+        out = torch.empty((T, n_q, D), dtype=torch.bfloat16, device=q.device)
+    pro = None
+    if prologue is not None:
+        p = prologue
+        for name in ("k", "v", "q_norm_w", "k_norm_w"):
+            _bits16(p[name], name)
+        if tuple(p["k"].shape) != (T, cd.n_kv_heads, D) or p["v"].shape != p["k"].shape:
+            raise ValueError("prologue k / v must be [T, n_kv, head_dim]")
+        cos, sin = p["cos"], p["sin"]
+        if cos.dtype != torch.float32 or tuple(cos.shape[1:]) != (D // 2,) or \
+                sin.shape != cos.shape:
+            raise ValueError("rope tables must be fp32 [max_pos, head_dim/2]")
+        pro = Prologue(p["q_norm_w"].data_ptr(), p["k_norm_w"].data_ptr(), float(p["eps"]),
+                       cos.data_ptr(), sin.data_ptr(), cos.shape[0], p["k"].data_ptr(),
+                       p["v"].data_ptr())
+    check(lib().pkv_attn_prefill(_ptr(q), n_q, _ptr(cu_seqlens), _ptr(slots), _ptr(start_pos),
+                                 n_seqs, T, int(max_seqlen_q_hint), pt, ctypes.byref(cd),
+                                 _ptr(k_pool), _ptr(v_pool), float(scale), int(window),
+                                 ctypes.byref(pro) if pro is not None else None, _ptr(out),
+                                 _ptr(lse), None, 0, _stream(stream, q.device)))
+    return out
+
+
+class PageAllocator:
+    """Host-side slot / page allocator (C++), see ``pkv_pt_*`` in the header."""
+
+    def __init__(self, n_pages, page_size, max_slots):
+        h = ctypes.c_void_p()
+        check(lib().pkv_pt_create(n_pages, page_size, max_slots, ctypes.byref(h)))
+        self._h = h
+        self.n_pages, self.page_size, self.max_slots = n_pages, page_size, max_slots
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib().pkv_pt_destroy(h)
+            self._h = None
+
+    @property
+    def pages_available(self):
+        return lib().pkv_pt_pages_available(self._h)
+
+    @property
+    def free_slot_count(self):
+        return lib().pkv_pt_free_slot_count(self._h)
+
+    def can_reserve(self, size, slot=None):
+        ok = ctypes.c_int32()
+        check(lib().pkv_pt_can_reserve(self._h, size, -1 if slot is None else slot,
+                                       ctypes.byref(ok)))
+        return bool(ok.value)
+
+    def allocate(self):
+        s = ctypes.c_int32()
+        st = lib().pkv_pt_allocate(self._h, ctypes.byref(s))
+        if st != 0:
+            raise PkvError(st, "no free slot")
+        return s.value
+
+    def reserve(self, slot, seq_len, dry_run=False):
+        ok = ctypes.c_int32()
+        st = lib().pkv_pt_reserve(self._h, slot, seq_len, int(dry_run), ctypes.byref(ok))
+        if st != 0:
+            raise PkvError(st, f"cannot reserve {seq_len} tokens in slot {slot} "
+                               f"({self.pages_available} pages free)")
+        return bool(ok.value)
+
+    def erase(self, slot):
+        check(lib().pkv_pt_erase(self._h, slot))
+
+    def capacity(self, slot):
+        return lib().pkv_pt_capacity(self._h, slot)
+
+    def row(self, slot):
+        n = lib().pkv_pt_row(self._h, slot, None, 0)
+        buf = (ctypes.c_int32 * max(n, 1))()
+        lib().pkv_pt_row(self._h, slot, buf, n)
+        return list(buf[:n])
+
+    def free_pages(self):
+        n = lib().pkv_pt_free_pages(self._h, None, 0)
+        buf = (ctypes.c_int32 * max(n, 1))()
+        lib().pkv_pt_free_pages(self._h, buf, n)
+        return list(buf[:n])
+
+    def export(self, pages_per_slot):
+        """Device-format table as an int32 CPU tensor ``[max_slots, pages_per_slot]``."""
+        t = torch.empty((self.max_slots, pages_per_slot), dtype=torch.int32)
+        check(lib().pkv_pt_export(self._h, ctypes.cast(t.data_ptr(),
+                                                       ctypes.POINTER(ctypes.c_int32)),
+                                  pages_per_slot))
+        return t

@@ -1,0 +1,272 @@
+// C-ABI entry points: host-side argument checks, then kernel launches.
+// Nothing here allocates, frees or synchronises device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pkv_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(PKV_ERR_LAUNCH, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
+  return PKV_OK;
+}
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int ilog2(int v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
+
+// Checks the cache descriptor and page table; fills the kernel-side geometry.
+pkv_status check_cache(const char* fn, const pkv_cache_desc* cd, const pkv_page_table& pt,
+                       bool allow_d512, pkv::PoolGeom* g, pkv::TableRef* tr) {
+  if (!cd) return fail(PKV_ERR_INVALID_ARG, "%s: cache descriptor is NULL", fn);
+  if (cd->n_pages < 2) return fail(PKV_ERR_INVALID_ARG, "%s: n_pages must be >= 2 (got %d)", fn, cd->n_pages);
+  if (!is_pow2(cd->page_size) || cd->page_size < 16 || cd->page_size > 256)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: page_size must be a power of two in [16, 256] (got %d)", fn,
+                cd->page_size);
+  const int D = cd->head_dim;
+  if (!(D == 64 || D == 128 || D == 256 || (allow_d512 && D == 512)))
+    return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d not supported", fn, D);
+  if (cd->n_kv_heads < 1) return fail(PKV_ERR_INVALID_ARG, "%s: n_kv_heads must be >= 1", fn);
+  if (!pt.table) return fail(PKV_ERR_INVALID_ARG, "%s: page table pointer is NULL", fn);
+  if (pt.max_slots < 2)
+    return fail(PKV_ERR_INVALID_ARG, "%s: max_slots must be >= 2 (slot 0 is reserved), got %d", fn,
+                pt.max_slots);
+  if (pt.pages_per_slot < 1)
+    return fail(PKV_ERR_INVALID_ARG, "%s: pages_per_slot must be >= 1", fn);
+  if ((long long)pt.pages_per_slot * cd->page_size > (1LL << 30))
+    return fail(PKV_ERR_INVALID_ARG, "%s: pages_per_slot * page_size exceeds 2^30 tokens", fn);
+  g->n_pages = cd->n_pages;
+  g->page_size = cd->page_size;
+  g->log2ps = ilog2(cd->page_size);
+  g->n_kv = cd->n_kv_heads;
+  g->head_dim = D;
+  tr->table = pt.table;
+  tr->max_slots = pt.max_slots;
+  tr->pps = pt.pages_per_slot;
+  return PKV_OK;
+}
+
+pkv_status check_heads(const char* fn, int n_q, int n_kv, int* G) {
+  if (n_q < 1 || n_q % n_kv != 0)
+    return fail(PKV_ERR_INVALID_ARG, "%s: n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                fn, n_q, n_kv);
+  *G = n_q / n_kv;
+  if (*G > 16)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: query heads per kv head must be <= 16 (got %d)", fn, *G);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+const char* pkv_version(void) { return "pkv 0.1.0 gfx950"; }
+
+pkv_status pkv_append(const void* k_new, const void* v_new, const int32_t* slot,
+                      const int32_t* pos, int32_t T, pkv_page_table pt,
+                      const pkv_cache_desc* cd, void* k_pool, void* v_pool, void* stream) {
+  const char* fn = "pkv_append";
+  if (T < 0) return fail(PKV_ERR_INVALID_ARG, "%s: T must be >= 0 (got %d)", fn, T);
+  pkv::PoolGeom g;
+  pkv::TableRef tr;
+  pkv_status st = check_cache(fn, cd, pt, true, &g, &tr);
+  if (st != PKV_OK) return st;
+  if (T == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot || !pos || !k_pool || !v_pool)
+    return fail(PKV_ERR_INVALID_ARG, "%s: NULL tensor pointer", fn);
+  pkv::AppendArgs a;
+  a.k_new = static_cast<const pkv::bf16_t*>(k_new);
+  a.v_new = static_cast<const pkv::bf16_t*>(v_new);
+  a.slot = slot;
+  a.pos = pos;
+  a.T = T;
+  a.pt = tr;
+  a.g = g;
+  a.kpool = static_cast<pkv::bf16_t*>(k_pool);
+  a.vpool = static_cast<pkv::bf16_t*>(v_pool);
+  return launched(pkv::launch_append(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+size_t pkv_decode_workspace_size(int32_t B, int32_t n_q_heads, int32_t n_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len_hint, int32_t window) {
+  if (B <= 0 || n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads != 0) return 0;
+  if (max_seq_len_hint < 1) max_seq_len_hint = 1;
+  return pkv::plan_decode(B, n_q_heads, n_kv_heads, head_dim, max_seq_len_hint,
+                          window > 0 ? window : 0)
+      .ws_bytes;
+}
+
+pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slots,
+                           const int32_t* seq_lens, int32_t B, int32_t max_seq_len_hint,
+                           pkv_page_table pt, const pkv_cache_desc* cd,
+                           const void* k_pool, const void* v_pool, float scale,
+                           int32_t window, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const char* fn = "pkv_attn_decode";
+  if (B < 0) return fail(PKV_ERR_INVALID_ARG, "%s: B must be >= 0 (got %d)", fn, B);
+  if (B > 65535) return fail(PKV_ERR_UNSUPPORTED, "%s: B must be <= 65535 (got %d)", fn, B);
+  pkv::PoolGeom g;
+  pkv::TableRef tr;
+  pkv_status st = check_cache(fn, cd, pt, true, &g, &tr);
+  if (st != PKV_OK) return st;
+  int G = 0;
+  st = check_heads(fn, n_q_heads, g.n_kv, &G);
+  if (st != PKV_OK) return st;
+  if (G * g.head_dim > 2048)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "%s: (n_q_heads / n_kv_heads) * head_dim must be <= 2048 (got %d * %d)", fn, G,
+                g.head_dim);
+  if (window < 0) return fail(PKV_ERR_INVALID_ARG, "%s: window must be >= 0", fn);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+  if (max_seq_len_hint < 1)
+    return fail(PKV_ERR_INVALID_ARG, "%s: max_seq_len_hint must be >= 1", fn);
+  if (B == 0) return PKV_OK;
+  if (!q || !slots || !seq_lens || !k_pool || !v_pool || !out)
+    return fail(PKV_ERR_INVALID_ARG, "%s: NULL tensor pointer", fn);
+  const pkv::DecodePlan plan =
+      pkv::plan_decode(B, n_q_heads, g.n_kv, g.head_dim, max_seq_len_hint, window);
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return fail(PKV_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", fn,
+                plan.ws_bytes, workspace ? workspace_bytes : (size_t)0);
+  pkv::DecodeArgs a;
+  a.q = static_cast<const pkv::bf16_t*>(q);
+  a.n_q = n_q_heads;
+  a.G = G;
+  a.slots = slots;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.pt = tr;
+  a.g = g;
+  a.kpool = static_cast<const pkv::bf16_t*>(k_pool);
+  a.vpool = static_cast<const pkv::bf16_t*>(v_pool);
+  a.scale_log2 = scale * pkv::kLog2eHost;
+  a.window = window;
+  a.split_tokens = plan.split_tokens;
+  a.max_splits = plan.max_splits;
+  a.part_o = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
+  a.part_ml = plan.ws_bytes ? static_cast<float*>(workspace) + plan.part_o_floats : nullptr;
+  a.out = static_cast<pkv::bf16_t*>(out);
+  a.lse = lse;
+  return launched(pkv::launch_decode(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+pkv_status pkv_attn_prefill(void* q, int32_t n_q_heads, const int32_t* cu_seqlens,
+                            const int32_t* slots, const int32_t* start_pos,
+                            int32_t n_seqs, int32_t total_tokens,
+                            int32_t max_seqlen_q_hint, pkv_page_table pt,
+                            const pkv_cache_desc* cd, void* k_pool, void* v_pool,
+                            float scale, int32_t window, const pkv_prologue* pro,
+                            void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  const char* fn = "pkv_attn_prefill";
+  if (n_seqs < 0 || total_tokens < 0)
+    return fail(PKV_ERR_INVALID_ARG, "%s: n_seqs and total_tokens must be >= 0", fn);
+  if (n_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "%s: n_seqs must be <= 65535", fn);
+  pkv::PoolGeom g;
+  pkv::TableRef tr;
+  pkv_status st = check_cache(fn, cd, pt, false, &g, &tr);
+  if (st != PKV_OK) return st;
+  int G = 0;
+  st = check_heads(fn, n_q_heads, g.n_kv, &G);
+  if (st != PKV_OK) return st;
+  if (window < 0) return fail(PKV_ERR_INVALID_ARG, "%s: window must be >= 0", fn);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+  if (max_seqlen_q_hint < 1)
+    return fail(PKV_ERR_INVALID_ARG, "%s: max_seqlen_q_hint must be >= 1", fn);
+  if (n_seqs == 0 || total_tokens == 0) return PKV_OK;
+  if (!q || !cu_seqlens || !slots || !k_pool || !v_pool || !out)
+    return fail(PKV_ERR_INVALID_ARG, "%s: NULL tensor pointer", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pro) {
+    if (!pro->q_norm_w || !pro->k_norm_w || !pro->rope_cos || !pro->rope_sin || !pro->k_raw ||
+        !pro->v_raw)
+      return fail(PKV_ERR_INVALID_ARG, "%s: NULL pointer in the prologue", fn);
+    if (pro->max_pos < 1) return fail(PKV_ERR_INVALID_ARG, "%s: prologue max_pos must be >= 1", fn);
+    if (!(pro->eps >= 0.f) || !std::isfinite(pro->eps))
+      return fail(PKV_ERR_INVALID_ARG, "%s: prologue eps must be finite and >= 0", fn);
+    pkv::PrologueArgs p;
+    p.q = static_cast<pkv::bf16_t*>(q);
+    p.k_raw = static_cast<const pkv::bf16_t*>(pro->k_raw);
+    p.v_raw = static_cast<const pkv::bf16_t*>(pro->v_raw);
+    p.q_w = static_cast<const pkv::bf16_t*>(pro->q_norm_w);
+    p.k_w = static_cast<const pkv::bf16_t*>(pro->k_norm_w);
+    p.eps = pro->eps;
+    p.cos_t = pro->rope_cos;
+    p.sin_t = pro->rope_sin;
+    p.max_pos = pro->max_pos;
+    p.n_q = n_q_heads;
+    p.T = total_tokens;
+    p.cu_seqlens = cu_seqlens;
+    p.slots = slots;
+    p.start_pos = start_pos;
+    p.n_seqs = n_seqs;
+    p.pt = tr;
+    p.g = g;
+    p.kpool = static_cast<pkv::bf16_t*>(k_pool);
+    p.vpool = static_cast<pkv::bf16_t*>(v_pool);
+    st = launched(pkv::launch_prologue(p, s), fn);
+    if (st != PKV_OK) return st;
+  }
+  pkv::PrefillArgs a;
+  a.q = static_cast<const pkv::bf16_t*>(q);
+  a.n_q = n_q_heads;
+  a.G = G;
+  a.cu_seqlens = cu_seqlens;
+  a.slots = slots;
+  a.start_pos = start_pos;
+  a.n_seqs = n_seqs;
+  a.pt = tr;
+  a.g = g;
+  a.kpool = static_cast<const pkv::bf16_t*>(k_pool);
+  a.vpool = static_cast<const pkv::bf16_t*>(v_pool);
+  a.scale_log2 = scale * pkv::kLog2eHost;
+  a.window = window;
+  a.q_tokens = pkv::prefill_q_tokens(G, g.head_dim);
+  a.n_qblocks = (max_seqlen_q_hint + a.q_tokens - 1) / a.q_tokens;
+  if (a.n_qblocks > 65535) a.n_qblocks = 65535;
+  a.out = static_cast<pkv::bf16_t*>(out);
+  a.lse = lse;
+  return launched(pkv::launch_prefill(a, s), fn);
+}
+
+pkv_status pkv_rope_table(float* cos_out, float* sin_out, int32_t max_pos, int32_t head_dim,
+                          double theta, void* stream) {
+  const char* fn = "pkv_rope_table";
+  if (!cos_out || !sin_out) return fail(PKV_ERR_INVALID_ARG, "%s: NULL output", fn);
+  if (max_pos < 1 || head_dim < 2 || head_dim % 2)
+    return fail(PKV_ERR_INVALID_ARG, "%s: need max_pos >= 1 and an even head_dim >= 2", fn);
+  if (!(theta > 0.0) || !std::isfinite(theta))
+    return fail(PKV_ERR_INVALID_ARG, "%s: theta must be finite and > 0", fn);
+  return launched(pkv::launch_rope_table(cos_out, sin_out, max_pos, head_dim, theta,
+                                         static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+// Internal host <-> kernel interface: argument blocks passed by value to the
+// kernels and the launchers each kernel file exports to the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef uint16_t bf16_t;
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+struct PoolGeom {
+  int n_pages;
+  int page_size;
+  int log2ps;
+  int n_kv;
+  int head_dim;
+};
+
+struct TableRef {
+  const int32_t* table;
+  int max_slots;
+  int pps;  // pages per slot (row stride)
+};
+
+struct AppendArgs {
+  const bf16_t* k_new;
+  const bf16_t* v_new;
+  const int32_t* slot;
+  const int32_t* pos;
+  int T;
+  TableRef pt;
+  PoolGeom g;
+  bf16_t* kpool;
+  bf16_t* vpool;
+};
+
+struct DecodeArgs {
+  const bf16_t* q;
+  int n_q;
+  int G;  // query heads per kv head
+  const int32_t* slots;
+  const int32_t* seq_lens;
+  int B;
+  TableRef pt;
+  PoolGeom g;
+  const bf16_t* kpool;
+  const bf16_t* vpool;
+  float scale_log2;  // softmax scale * log2(e)
+  int window;
+  int split_tokens;  // keys per split (multiple of 128)
+  int max_splits;    // grid extent; 1 = no workspace, write out directly
+  float* part_o;     // [B][n_kv][max_splits][G][D]
+  float* part_ml;    // [B][n_kv][max_splits][G][2]  (running max in log2 units, sum)
+  bf16_t* out;       // [B][n_q][D]
+  float* lse;        // [B][n_q] or null
+};
+
+struct PrologueArgs {
+  bf16_t* q;  // [T][n_q][D], rewritten in place
+  const bf16_t* k_raw;
+  const bf16_t* v_raw;
+  const bf16_t* q_w;
+  const bf16_t* k_w;
+  float eps;
+  const float* cos_t;
+  const float* sin_t;
+  int max_pos;
+  int n_q;
+  int T;
+  const int32_t* cu_seqlens;
+  const int32_t* slots;
+  const int32_t* start_pos;  // may be null
+  int n_seqs;
+  TableRef pt;
+  PoolGeom g;
+  bf16_t* kpool;
+  bf16_t* vpool;
+};
+
+struct PrefillArgs {
+  const bf16_t* q;  // [T][n_q][D]
+  int n_q;
+  int G;
+  const int32_t* cu_seqlens;
+  const int32_t* slots;
+  const int32_t* start_pos;  // may be null
+  int n_seqs;
+  TableRef pt;
+  PoolGeom g;
+  const bf16_t* kpool;
+  const bf16_t* vpool;
+  float scale_log2;
+  int window;
+  int q_tokens;   // query tokens per workgroup
+  int n_qblocks;  // grid extent over query blocks (grid-stride beyond it)
+  bf16_t* out;
+  float* lse;
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_prologue(const PrologueArgs& a, hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_rope_table(float* c, float* s, int max_pos, int head_dim, double theta,
+                             hipStream_t st);
+
+// Split-K plan for decode (host): keys per split and grid extent.
+struct DecodePlan {
+  int split_tokens;
+  int max_splits;
+  size_t ws_bytes;
+  size_t part_o_floats;  // offset of part_ml in floats
+};
+DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_hint,
+                       int window);
+
+// Query tokens per prefill workgroup for a GQA ratio.
+int prefill_q_tokens(int G, int head_dim);
+
+}  // namespace pkv

@@ -1,0 +1,151 @@
+"""GPU decode parity against the fp64 oracle, plus exact GPU-side invariants."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_attention_pagetable_amd as pkv
+from synth import CONFIGS, config_lengths, make_decode_case
+from tests.gpu_util import (assert_attn_close, dev_i32, gpu_decode_setup, host_bits, host_f64,
+                            oracle_decode_pools, run_gpu_decode)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (n_q, n_kv, D, ps, lengths, window, scale)
+    "tiny": (4, 2, 64, 16, [37, 50], 0, 1 / 8),
+    "tiny_w20": (4, 2, 64, 16, [37, 50], 20, 1 / 8),
+    "d128_g4_edges": (32, 8, 128, 128, [1, 127, 128, 129, 0, 700, 1024, 31], 0, None),
+    "d128_g3_ps64": (24, 8, 128, 64, [3000, 5, 0, 1, 2049, 640], 0, None),
+    "d128_ps16": (8, 2, 128, 16, [300, 17, 16, 1000], 0, None),
+    "d256_w512": (8, 2, 256, 64, [256, 511, 512, 513, 1536, 900], 512, None),
+    "d512_full": (8, 2, 512, 64, [256, 1536, 777], 0, None),
+    "g1": (8, 8, 128, 128, [500, 1], 0, None),
+    "g16": (16, 1, 64, 32, [200, 33], 0, None),
+    "w1": (4, 2, 64, 16, [37, 50], 1, None),
+}
+
+
+def _run(name, seed=0):
+    n_q, n_kv, D, ps, lengths, window, scale = CASES[name]
+    case = make_decode_case(n_q, n_kv, D, ps, lengths, max_slots=len(lengths) + 2,
+                            seed=1000 + seed + D, window=window, scale=scale, spare_pages=2)
+    kp, vp, table = gpu_decode_setup(case)
+    out, lse = run_gpu_decode(case, kp, vp, table)
+    return case, kp, vp, table, out, lse
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_matches_oracle(name):
+    case, kp, vp, table, out, lse = _run(name)
+    okp, ovp = oracle_decode_pools(case)
+    ref, ref_lse = oracle.attn_decode(case.q, okp, ovp, case.table, case.slots, case.seq_lens,
+                                      case.scale, case.window)
+    assert_attn_close(host_f64(out), ref, name)
+    g_lse = lse.cpu().numpy().astype(np.float64)
+    idle = case.seq_lens == 0
+    assert np.all(np.isneginf(g_lse[idle]))
+    assert np.max(np.abs(g_lse[~idle] - ref_lse[~idle])) <= 1e-3
+    # idle rows are exactly zero
+    assert np.all(host_bits(out)[idle] == 0)
+
+
+def test_decode_length_one_returns_v_exactly():
+    case = make_decode_case(8, 2, 128, 16, [1, 1, 1], max_slots=5, seed=3)
+    kp, vp, table = gpu_decode_setup(case)
+    out, _ = run_gpu_decode(case, kp, vp, table, hint=1)
+    want = np.repeat(case.v_new, 4, axis=1)   # head h reads kv head h // 4
+    assert np.array_equal(host_bits(out), want)
+
+
+def test_decode_bitwise_deterministic_and_page_permutation_invariant():
+    n_q, n_kv, D, ps, lengths, window, scale = CASES["d128_g3_ps64"]
+    case = make_decode_case(n_q, n_kv, D, ps, lengths, max_slots=8, seed=77, spare_pages=5)
+    kp, vp, table = gpu_decode_setup(case)
+    o1, l1 = run_gpu_decode(case, kp, vp, table, hint=3000)
+    o2, l2 = run_gpu_decode(case, kp, vp, table, hint=3000)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    # relabel physical pages: same logical content, different page ids
+    rng = np.random.default_rng(4)
+    relabel = np.concatenate([[0], 1 + rng.permutation(case.n_pages - 1)]).astype(np.int64)
+    kp2 = torch.empty_like(kp)
+    vp2 = torch.empty_like(vp)
+    idx = torch.from_numpy(relabel).to(kp.device)
+    kp2[idx] = kp
+    vp2[idx] = vp
+    t2 = np.where(case.table > 0, relabel[np.maximum(case.table, 0)], case.table).astype(np.int32)
+    o3, l3 = run_gpu_decode(case, kp2, vp2, dev_i32(t2), hint=3000)
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16)) and torch.equal(l1, l3)
+
+
+def test_decode_window_at_least_length_equals_full_bitwise():
+    case = make_decode_case(8, 2, 128, 64, [300, 77, 512], max_slots=5, seed=9)
+    kp, vp, table = gpu_decode_setup(case)
+    full, _ = run_gpu_decode(case, kp, vp, table, hint=512)
+    case.window = 512
+    win, _ = run_gpu_decode(case, kp, vp, table, hint=512)
+    assert torch.equal(full.view(torch.int16), win.view(torch.int16))
+
+
+def test_decode_hint_below_lengths_still_correct():
+    case = make_decode_case(8, 2, 128, 128, [2000, 700], max_slots=4, seed=12)
+    kp, vp, table = gpu_decode_setup(case)
+    out, _ = run_gpu_decode(case, kp, vp, table, hint=256)   # plan sized for 256 keys
+    okp, ovp = oracle_decode_pools(case)
+    ref, _ = oracle.attn_decode(case.q, okp, ovp, case.table, case.slots, case.seq_lens,
+                                case.scale, 0)
+    assert_attn_close(host_f64(out), ref, "hint<L")
+
+
+# ---- full-size workloads, sampled rows, in the bench's launch configuration ----
+
+def _full_case(name, layer_dim=None, window=0, salt=0):
+    c = CONFIGS[name]
+    L, slots = config_lengths(name, salt)
+    D = layer_dim or c["head_dim"]
+    case = make_decode_case(c["n_q"], c["n_kv"], D, c["page_size"], L,
+                            max_slots=c["max_slots"], seed=3407 + c["index"] + salt,
+                            slot_of_row=slots, window=window, spare_pages=4,
+                            pages_per_slot=-(-c["len_hi"] // c["page_size"]))
+    return case, c["len_hi"]
+
+
+def _sampled_check(case, hint, n_rows=6):
+    kp, vp, table = gpu_decode_setup(case)
+    out, lse = run_gpu_decode(case, kp, vp, table, hint=hint)
+    assert torch.isfinite(out.float()).all()
+    rng = np.random.default_rng(5)
+    rows = rng.choice(case.B, size=min(n_rows, case.B), replace=False)
+    g = host_f64(out)
+    for b in rows:
+        L = int(case.seq_lens[b])
+        if L == 0:
+            assert np.all(g[b] == 0)
+            continue
+        K = oracle.bf16_bits_to_f64(np.concatenate([case.hist_k[b], case.k_new[b:b + 1]]))
+        V = oracle.bf16_bits_to_f64(np.concatenate([case.hist_v[b], case.v_new[b:b + 1]]))
+        ref, _ = oracle.attend_rows(oracle.bf16_bits_to_f64(case.q[b]), K, V, L - 1,
+                                    case.scale, case.window)
+        assert_attn_close(g[b], ref, f"row {b}")
+    idle = np.nonzero(case.seq_lens == 0)[0]
+    assert np.all(host_bits(out)[idle] == 0)
+
+
+def test_full_qwen3_decode_sampled():
+    case, hint = _full_case("qwen3_decode")
+    _sampled_check(case, hint)
+
+
+def test_full_llama_decode_sampled():
+    case, hint = _full_case("llama_decode")
+    assert (case.seq_lens == 0).sum() == 6
+    _sampled_check(case, hint)
+
+
+def test_full_gemma_sliding_and_full_layers_sampled():
+    c = CONFIGS["gemma_mixed"]
+    case, hint = _full_case("gemma_mixed", layer_dim=c["sliding_dim"], window=c["window"])
+    _sampled_check(case, hint)
+    case, hint = _full_case("gemma_mixed", layer_dim=c["full_dim"])
+    _sampled_check(case, hint)

@@ -1,0 +1,161 @@
+"""GPU prefill parity (with and without the fused prologue) against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_attention_pagetable_amd as pkv
+from synth import CONFIGS, config_lengths, make_prefill_case
+from tests.gpu_util import (assert_attn_close, dev_bits, dev_i32, gpu_pools, host_bits,
+                            host_f64)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (n_q, n_kv, D, ps, lengths, start_pos, window)
+    "tiny": (4, 2, 64, 16, [37, 50], None, 0),
+    "tiny_w20": (4, 2, 64, 16, [37, 50], None, 20),
+    "d128_g4_ragged": (32, 8, 128, 128, [1, 33, 130, 7, 257], None, 0),
+    "d128_g4_prefix": (32, 8, 128, 128, [40, 100, 3], [5, 128, 300], 0),
+    "d128_g3": (24, 8, 128, 64, [70, 1, 200], None, 0),
+    "d256_w64": (8, 2, 256, 64, [300, 45], [0, 20], 64),
+    "g1_ps16": (4, 4, 128, 16, [90, 31], None, 0),
+    "g16": (16, 1, 64, 32, [40, 9], None, 0),
+    "slot0_pad": (8, 2, 64, 16, [20, 12, 30], None, 0),
+}
+
+
+def _pools_with_prefix(case):
+    """Device + oracle pools holding each sequence's cached prefix."""
+    kp, vp = gpu_pools(case)
+    okp, ovp = case.empty_pools()
+    table = dev_i32(case.table)
+    pk, pv, ps_, pp = case.prefix_tokens()
+    if len(ps_):
+        pkv.append(dev_bits(pk), dev_bits(pv), dev_i32(ps_), dev_i32(pp), table, kp, vp)
+        oracle.append(okp, ovp, case.table, pk, pv, ps_, pp)
+    return kp, vp, table, okp, ovp
+
+
+def _case(name, seed=0):
+    n_q, n_kv, D, ps, lengths, sp, window = CASES[name]
+    slots = None
+    if name == "slot0_pad":
+        slots = [1, 0, 2]   # a padding sequence in slot 0
+    return make_prefill_case(n_q, n_kv, D, ps, lengths, seed=2000 + seed + D, start_pos=sp,
+                             slots=slots, max_slots=4 if slots else None, window=window)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_prefill_no_prologue_matches_oracle(name):
+    case = _case(name)
+    kp, vp, table, okp, ovp = _pools_with_prefix(case)
+    tsl, tpos = case.token_slots(), case.token_pos()
+    pkv.append(dev_bits(case.k), dev_bits(case.v), dev_i32(tsl), dev_i32(tpos), table, kp, vp)
+    oracle.append(okp, ovp, case.table, case.k, case.v, tsl, tpos)
+    q = dev_bits(case.q)
+    lse = torch.empty((case.T, case.n_q), dtype=torch.float32, device=q.device)
+    out = pkv.attn_prefill(q, dev_i32(case.cu_seqlens), dev_i32(case.slots), table, kp, vp,
+                           scale=case.scale, window=case.window,
+                           start_pos=dev_i32(case.start_pos),
+                           max_seqlen_q_hint=int(np.diff(case.cu_seqlens).max()), lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.attn_prefill(case.q, okp, ovp, case.table, case.cu_seqlens,
+                                       case.slots, case.start_pos, case.scale, case.window)
+    assert_attn_close(host_f64(out), ref, name)
+    g_lse = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(ref_lse)
+    assert np.all(np.isneginf(g_lse[~fin]))
+    assert np.max(np.abs(g_lse[fin] - ref_lse[fin]), initial=0.0) <= 1e-3
+    # q untouched without a prologue; padding rows exactly zero
+    assert np.array_equal(host_bits(q), case.q)
+    pad = tsl == 0
+    assert np.all(host_bits(out)[pad] == 0)
+
+
+def _run_with_prologue(case, kp, vp, table, hint=None):
+    D = case.head_dim
+    max_pos = int((case.start_pos + np.diff(case.cu_seqlens)).max()) + 1
+    cos, sin = pkv.rope_table(max_pos, D, case.theta)
+    q = dev_bits(case.q)
+    pro = dict(q_norm_w=dev_bits(case.q_norm_w), k_norm_w=dev_bits(case.k_norm_w),
+               eps=case.eps, cos=cos, sin=sin, k=dev_bits(case.k), v=dev_bits(case.v))
+    out = pkv.attn_prefill(q, dev_i32(case.cu_seqlens), dev_i32(case.slots), table, kp, vp,
+                           scale=case.scale, window=case.window,
+                           start_pos=dev_i32(case.start_pos),
+                           max_seqlen_q_hint=hint or int(np.diff(case.cu_seqlens).max()),
+                           prologue=pro)
+    torch.cuda.synchronize()
+    return q, out
+
+
+def _oracle_with_prologue(case, okp, ovp):
+    tsl, tpos = case.token_slots(), case.token_pos()
+    q2, k2, v = oracle.prologue_qwen3(case.q, case.k, case.v, case.q_norm_w, case.k_norm_w,
+                                      tpos, case.eps, case.theta)
+    q2b, k2b = oracle.f64_to_bf16_bits(q2), oracle.f64_to_bf16_bits(k2)
+    oracle.append(okp, ovp, case.table, k2b, case.v, tsl, tpos)
+    return q2, q2b, k2
+
+
+@pytest.mark.parametrize("name", ["tiny", "d128_g4_ragged", "d128_g4_prefix", "d256_w64",
+                                  "slot0_pad"])
+def test_prefill_with_prologue_matches_oracle(name):
+    case = _case(name, seed=7)
+    kp, vp, table, okp, ovp = _pools_with_prefix(case)
+    q, out = _run_with_prologue(case, kp, vp, table)
+    q2, q2b, k2 = _oracle_with_prologue(case, okp, ovp)
+    tsl = case.token_slots()
+    live = tsl != 0
+    # q' in place: within tolerance of the fp64 value and (almost always) the nearest bf16
+    gq = host_f64(q)
+    assert_attn_close(gq[live], q2[live], "q'")
+    ulp_ok = np.mean(host_bits(q)[live] == q2b[live])
+    assert ulp_ok >= 0.99, f"only {ulp_ok:.4f} of q' match the RNE-rounded fp64 value"
+    # the K pool holds k' (same tolerance), the V pool the raw v bit for bit
+    gk = host_bits(kp)
+    okb = okp
+    written = okb != 0xFFFF
+    assert np.array_equal(gk == 0xFFFF, ~written), "K rows written at the wrong places"
+    kd = oracle.bf16_bits_to_f64(gk[written]) - oracle.bf16_bits_to_f64(okb[written])
+    assert np.max(np.abs(kd)) <= 2e-2
+    assert np.array_equal(host_bits(vp), ovp)
+    ref, _ = oracle.attn_prefill(q2b, okp, ovp, case.table, case.cu_seqlens, case.slots,
+                                 case.start_pos, case.scale, case.window)
+    assert_attn_close(host_f64(out), ref, name)
+
+
+def test_rope_table_matches_fp64():
+    D, theta, max_pos = 128, 1e6, 4096
+    c, s = pkv.rope_table(max_pos, D, theta)
+    torch.cuda.synchronize()
+    inv = oracle.rope_inv_freq(D, theta)
+    ang = np.arange(max_pos)[:, None] * inv[None, :]
+    assert np.max(np.abs(c.cpu().numpy() - np.cos(ang))) <= 1e-7
+    assert np.max(np.abs(s.cpu().numpy() - np.sin(ang))) <= 1e-7
+
+
+def test_full_qwen3_prefill_sampled():
+    """The 16-prompt workload with the prologue, sampled token rows vs the oracle."""
+    c = CONFIGS["qwen3_prefill"]
+    L, slots = config_lengths("qwen3_prefill")
+    case = make_prefill_case(c["n_q"], c["n_kv"], c["head_dim"], c["page_size"], L,
+                             seed=3407 + c["index"], slots=slots, max_slots=c["max_slots"],
+                             eps=c["eps"], theta=c["theta"], spare_pages=4,
+                             pages_per_slot=-(-c["len_hi"] // c["page_size"]))
+    kp, vp = gpu_pools(case)
+    table = dev_i32(case.table)
+    q, out = _run_with_prologue(case, kp, vp, table, hint=c["len_hi"])
+    assert torch.isfinite(out.float()).all()
+    okp, ovp = case.empty_pools()
+    q2, q2b, _ = _oracle_with_prologue(case, okp, ovp)
+    rng = np.random.default_rng(11)
+    rows = np.sort(rng.choice(case.T, size=12, replace=False))
+    g = host_f64(out)
+    for t in rows:
+        n = int(np.searchsorted(case.cu_seqlens, t, side="right") - 1)
+        p = t - int(case.cu_seqlens[n])
+        K, V = oracle.gather_kv(okp, ovp, case.table, int(case.slots[n]), p + 1)
+        ref, _ = oracle.attend_rows(oracle.bf16_bits_to_f64(q2b[t]), K, V, p, case.scale, 0)
+        assert_attn_close(g[t], ref, f"token {t}")
