@@ -1,0 +1,456 @@
+#!/usr/bin/env python3
+"""Throughput bench of the paged KV-cache attention path on one MI355X.
+
+Default workload (``qwen3_decode``): a Qwen3-4B-shaped decode step -- 8 active
+slots of 9 (slot 0 reserved), 32 query / 8 kv heads, head_dim 128, page 128,
+context lengths U[64, 1024], 36 layers each with its own K/V pools.  One step
+= for every layer: append the new token's K/V into the pages, then split-K
+decode attention (+ log-sum-exp merge).  A second timed phase runs the
+Qwen3-4B-shaped chunked prefill (16 prompts U[32, 512], fused q/k RMSNorm +
+RoPE + append prologue, then MFMA prefill attention, 36 layers) and is
+reported under ``prefill``.
+
+Both phases are captured once in a HIP graph (through torch.cuda.CUDAGraph) and
+replayed: inputs are resident in HBM before the timed region, and the timed
+region is bracketed by torch.cuda.synchronize().  Kernel-level durations for
+the roofline come from HIP events around graphs that hold only the attention
+calls, on the stream the kernels run on.
+
+Prints ONE JSON line.  ``--gpus`` above 1 is refused: this path runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn HBM GB/s (% peak) + prefill attn TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "paged_kv_attention_pagetable_amd", "csrc")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------
+
+class DecodeWorkload:
+    """Per-layer pools with history already appended; one shared page table."""
+
+    def __init__(self, name, device="cuda"):
+        import torch
+
+        import paged_kv_attention_pagetable_amd as pkv
+        from synth import CONFIGS, config_lengths, make_decode_case
+        from synth.device import DeviceRandom
+
+        self.pkv, self.torch = pkv, torch
+        c = CONFIGS[name]
+        self.name, self.c = name, c
+        lengths, slots = config_lengths(name)
+        ps = c["page_size"]
+        pps = -(-c["len_hi"] // ps)
+        if name == "gemma_mixed":
+            kinds = [(c["sliding_dim"], c["window"]), (c["full_dim"], 0)] * c["layers"]
+        else:
+            kinds = [(c["head_dim"], c.get("window", 0))] * c["layers"]
+        base = make_decode_case(c["n_q"], c["n_kv"], kinds[0][0], ps, lengths,
+                                max_slots=c["max_slots"], seed=3407 + c["index"],
+                                slot_of_row=slots, pages_per_slot=pps, with_history=False)
+        self.case = base
+        self.hint = c["len_hi"]
+        dev = device
+        self.table = torch.from_numpy(base.table).to(dev)
+        self.slots = torch.from_numpy(base.slots).to(dev)
+        self.seq_lens = torch.from_numpy(base.seq_lens).to(dev)
+        self.aslots = torch.from_numpy(base.append_slots()).to(dev)
+        self.apos = torch.from_numpy(base.append_pos()).to(dev)
+        hist_slot, hist_pos = [], []
+        for b in range(base.B):
+            n = max(int(base.seq_lens[b]) - 1, 0)
+            hist_slot.append(np.full(n, base.slots[b], np.int32))
+            hist_pos.append(np.arange(n, dtype=np.int32))
+        hs = torch.from_numpy(np.concatenate(hist_slot)).to(dev)
+        hp = torch.from_numpy(np.concatenate(hist_pos)).to(dev)
+        rnd = DeviceRandom(3407 + 100 * c["index"], dev)
+        B, n_q, n_kv = base.B, c["n_q"], c["n_kv"]
+        self.layers = []
+        for D, window in kinds:
+            kp, vp = pkv.new_pools(base.n_pages, n_kv, ps, D, dev, fill=-1)
+            pkv.append(rnd.bf16((hs.numel(), n_kv, D)), rnd.bf16((hs.numel(), n_kv, D)), hs, hp,
+                       self.table, kp, vp)
+            ws_bytes = pkv.decode_workspace_size(B, n_q, n_kv, D, self.hint, window)
+            self.layers.append(dict(
+                D=D, window=window, kp=kp, vp=vp, q=rnd.bf16((B, n_q, D)),
+                k_new=rnd.bf16((B, n_kv, D)), v_new=rnd.bf16((B, n_kv, D)),
+                out=torch.empty((B, n_q, D), dtype=torch.bfloat16, device=dev),
+                ws=pkv.new_decode_workspace(ws_bytes, dev),
+                scale=1.0 / math.sqrt(D)))
+        torch.cuda.synchronize()
+        self.n_calls = len(self.layers)
+
+    def attn(self, ly, fused_append=False):
+        self.pkv.attn_decode(ly["q"], self.slots, self.seq_lens, self.table, ly["kp"], ly["vp"],
+                             scale=ly["scale"], window=ly["window"], max_seq_len_hint=self.hint,
+                             out=ly["out"], workspace=ly["ws"],
+                             k_new=ly["k_new"] if fused_append else None,
+                             v_new=ly["v_new"] if fused_append else None)
+
+    def step(self):
+        """Every layer: append the new token's K/V, then attend (one fused kernel)."""
+        for ly in self.layers:
+            self.attn(ly, fused_append=True)
+
+    def attn_only(self):
+        for ly in self.layers:
+            self.attn(ly)
+
+    def attn_bytes(self, ly):
+        """Algorithmic HBM bytes of one attention call: visible K/V rows, Q, O, page ids."""
+        c, case = self.c, self.case
+        L = case.seq_lens.astype(np.int64)
+        if ly["window"] > 0:
+            L = np.minimum(L, ly["window"])
+        kv = int(L.sum()) * c["n_kv"] * ly["D"] * 2 * 2
+        active = int((case.seq_lens > 0).sum())
+        qo = active * c["n_q"] * ly["D"] * 2 * 2
+        pages = int(np.ceil(L / case.page_size).sum()) * 4
+        return kv + qo + pages
+
+    def append_bytes(self, ly):
+        active = int((self.case.seq_lens > 0).sum())
+        return active * self.c["n_kv"] * ly["D"] * 2 * 2 * 2   # read + write, K and V
+
+    def describe(self):
+        c, case = self.c, self.case
+        d = dict(workload=self.name, batch=int(case.B), active=int((case.seq_lens > 0).sum()),
+                 n_q=c["n_q"], n_kv=c["n_kv"], page_size=c["page_size"],
+                 layers=len(self.layers), head_dims=sorted({ly["D"] for ly in self.layers}),
+                 context=f"U[{c['len_lo']},{c['len_hi']}]",
+                 mean_context=float(case.seq_lens[case.seq_lens > 0].mean()))
+        if any(ly["window"] for ly in self.layers):
+            d["window"] = max(ly["window"] for ly in self.layers)
+        return d
+
+
+class PrefillWorkload:
+    def __init__(self, device="cuda"):
+        import torch
+
+        import paged_kv_attention_pagetable_amd as pkv
+        from synth import CONFIGS, config_lengths, make_prefill_case
+        from synth.device import DeviceRandom
+
+        self.pkv, self.torch = pkv, torch
+        c = CONFIGS["qwen3_prefill"]
+        self.c = c
+        lengths, slots = config_lengths("qwen3_prefill")
+        ps, D = c["page_size"], c["head_dim"]
+        case = make_prefill_case(c["n_q"], c["n_kv"], D, ps, lengths, seed=3407 + c["index"],
+                                 slots=slots, max_slots=c["max_slots"],
+                                 pages_per_slot=-(-c["len_hi"] // ps))
+        self.case = case
+        dev = device
+        self.table = torch.from_numpy(case.table).to(dev)
+        self.slots = torch.from_numpy(case.slots).to(dev)
+        self.cu = torch.from_numpy(case.cu_seqlens).to(dev)
+        self.start = torch.from_numpy(case.start_pos).to(dev)
+        self.cos, self.sin = pkv.rope_table(c["len_hi"] + 1, D, c["theta"], dev)
+        rnd = DeviceRandom(3407 + 100 * c["index"], dev)
+        T = case.T
+        self.layers = []
+        for _ in range(c["layers"]):
+            kp, vp = pkv.new_pools(case.n_pages, c["n_kv"], ps, D, dev, fill=-1)
+            self.layers.append(dict(
+                kp=kp, vp=vp, q=rnd.bf16((T, c["n_q"], D)), k=rnd.bf16((T, c["n_kv"], D)),
+                v=rnd.bf16((T, c["n_kv"], D)), qw=rnd.bf16((D,), 1.0, 0.1),
+                kw=rnd.bf16((D,), 1.0, 0.1),
+                out=torch.empty((T, c["n_q"], D), dtype=torch.bfloat16, device=dev)))
+        torch.cuda.synchronize()
+        self.n_calls = len(self.layers)
+        self.scale = 1.0 / math.sqrt(D)
+
+    def _call(self, ly, with_prologue):
+        pro = None
+        if with_prologue:
+            pro = dict(q_norm_w=ly["qw"], k_norm_w=ly["kw"], eps=self.c["eps"], cos=self.cos,
+                       sin=self.sin, k=ly["k"], v=ly["v"])
+        self.pkv.attn_prefill(ly["q"], self.cu, self.slots, self.table, ly["kp"], ly["vp"],
+                              scale=self.scale, start_pos=self.start,
+                              max_seqlen_q_hint=self.c["len_hi"], prologue=pro, out=ly["out"])
+
+    def step(self):
+        for ly in self.layers:
+            self._call(ly, True)
+
+    def attn_only(self):
+        for ly in self.layers:
+            self._call(ly, False)
+
+    def flops_per_call(self):
+        """Causal attention FLOPs: 2 (QK^T) + 2 (PV) per visible (query, key) pair."""
+        L = np.diff(self.case.cu_seqlens).astype(np.int64)
+        c = self.c
+        return int((2 * 2 * c["head_dim"] * c["n_q"] * L * (L + 1) // 2).sum())
+
+    def prologue_bytes(self):
+        c, T = self.c, self.case.T
+        rows = T * (c["n_q"] + 2 * c["n_kv"])
+        return rows * c["head_dim"] * 2 * 2   # read + write
+
+    def describe(self):
+        c, case = self.c, self.case
+        return dict(workload="qwen3_prefill", prompts=len(case.slots), tokens=case.T,
+                    n_q=c["n_q"], n_kv=c["n_kv"], head_dim=c["head_dim"],
+                    page_size=c["page_size"], layers=c["layers"],
+                    lengths=f"U[{c['len_lo']},{c['len_hi']}]", prologue="rmsnorm+rope theta 1e6")
+
+
+# ----------------------------------------------------------------------------
+# timing
+# ----------------------------------------------------------------------------
+
+def capture(fn):
+    import torch
+    fn()                       # eager warm-up: no allocation happens inside fn
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, reps, warmup):
+    import torch
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps   # ms per replay
+
+
+def source_sha(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(tag, sources, launches_per_call=1):
+    """HBM bytes per call from a committed rocprofv3 PMC summary, if current."""
+    path = os.path.join(PROFILES, f"{tag}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != source_sha(sources):
+        return None   # kernel changed since the counters were taken
+    return rec.get("hbm_bytes_per_call")
+
+
+# ----------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample)
+# ----------------------------------------------------------------------------
+
+def cpu_decode_baseline(seconds):
+    import oracle
+    from synth import CONFIGS, config_lengths, make_decode_case
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    c = CONFIGS["qwen3_decode"]
+    lengths, slots = config_lengths("qwen3_decode")
+    case = make_decode_case(c["n_q"], c["n_kv"], c["head_dim"], c["page_size"], lengths,
+                            max_slots=c["max_slots"], seed=3407 + c["index"], slot_of_row=slots,
+                            pages_per_slot=-(-c["len_hi"] // c["page_size"]))
+    kp, vp = case.empty_pools()
+    hk, hv, hs, hp = case.history_tokens()
+    oracle.append(kp, vp, case.table, hk, hv, hs, hp)
+    per_call = (int(case.seq_lens.sum()) * c["n_kv"] * c["head_dim"] * 4
+                + case.B * c["n_q"] * c["head_dim"] * 4)
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        n, t0 = 0, time.perf_counter()
+        while True:
+            oracle.append(kp, vp, case.table, case.k_new, case.v_new, case.append_slots(),
+                          case.append_pos())
+            oracle.attn_decode(case.q, kp, vp, case.table, case.slots, case.seq_lens,
+                               case.scale, 0)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    return dict(value=round(n * per_call / el / 1e9, 6), unit="GB/s", cores=1, kind="oracle",
+                sample=f"{n} qwen3_decode layer calls (8 rows, append + attention, "
+                       f"fp64 numpy, 1 BLAS thread) in {el:.1f} s",
+                seconds=round(el, 2))
+
+
+def cpu_prefill_baseline(seconds):
+    import oracle
+    from synth import CONFIGS, config_lengths, make_prefill_case
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    c = CONFIGS["qwen3_prefill"]
+    lengths, slots = config_lengths("qwen3_prefill")
+    case = make_prefill_case(c["n_q"], c["n_kv"], c["head_dim"], c["page_size"], lengths,
+                             seed=3407 + c["index"], slots=slots, max_slots=c["max_slots"],
+                             pages_per_slot=-(-c["len_hi"] // c["page_size"]))
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    flops, t0 = 0, time.perf_counter()
+    try:
+        kp, vp = case.empty_pools()
+        tsl, tpos = case.token_slots(), case.token_pos()
+        q2, k2, v = oracle.prologue_qwen3(case.q, case.k, case.v, case.q_norm_w, case.k_norm_w,
+                                          tpos, case.eps, case.theta)
+        oracle.append(kp, vp, case.table, oracle.f64_to_bf16_bits(k2), case.v, tsl, tpos)
+        qb = oracle.f64_to_bf16_bits(q2)
+        done = 0
+        for n in range(len(case.slots)):
+            a, b = int(case.cu_seqlens[n]), int(case.cu_seqlens[n + 1])
+            K, V = oracle.gather_kv(kp, vp, case.table, int(case.slots[n]), b - a)
+            for t in range(a, b):
+                p = t - a
+                oracle.attend_rows(oracle.bf16_bits_to_f64(qb[t]), K[: p + 1], V[: p + 1], p,
+                                   case.scale, 0)
+                flops += 4 * c["head_dim"] * c["n_q"] * (p + 1)
+                done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        el = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    return dict(value=round(flops / el / 1e12, 9), unit="TFLOP/s", cores=1, kind="oracle",
+                sample=f"prologue + append of all {case.T} tokens, then attention of the first "
+                       f"{done} query tokens (fp64 numpy, 1 BLAS thread) in {el:.1f} s",
+                seconds=round(el, 2))
+
+
+# ----------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_decode",
+                    choices=["qwen3_decode", "llama_decode", "gemma_mixed"])
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--kernel-reps", type=int, default=20,
+                    help="replays of the attention-only graphs for kernel timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this bench runs the single-GPU path only; "
+                                   f"--gpus {args.gpus} is not supported (use --gpus 1)"}))
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    import paged_kv_attention_pagetable_amd as pkv
+    pkv.lib()
+
+    log(f"setting up {args.workload}")
+    wl = DecodeWorkload(args.workload)
+    g_step = capture(wl.step)
+    g_attn = capture(wl.attn_only)
+    log("timing decode step")
+    torch.cuda.synchronize()
+    ms_step = time_graph(g_step, args.steps, args.warmup)
+    ms_attn = time_graph(g_attn, args.kernel_reps, 2) / wl.n_calls
+    attn_bytes = [wl.attn_bytes(ly) for ly in wl.layers]
+    step_bytes = sum(attn_bytes) + sum(wl.append_bytes(ly) for ly in wl.layers)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = (sum(attn_bytes) / wl.n_calls) / (ms_attn * 1e-3) / 1e9
+    dec_sources = ["decode.hip", "pkv_device.h", "pkv_internal.h"]
+    traffic = pmc_traffic(f"decode_{args.workload}", dec_sources)
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                    kernel="decode attention (split-K + in-kernel LSE merge)",
+                    algorithmic_bytes_per_call=int(sum(attn_bytes) / wl.n_calls),
+                    us_per_call=round(ms_attn * 1e3, 3))
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, random page permutation)",
+        "config": wl.describe(), "roofline": roofline,
+    }
+    del g_step, g_attn
+
+    if not args.no_prefill:
+        log("setting up qwen3_prefill")
+        pw = PrefillWorkload()
+        gp_step = capture(pw.step)
+        gp_attn = capture(pw.attn_only)
+        log("timing prefill")
+        ms_p = time_graph(gp_step, args.steps, args.warmup)
+        ms_pa = time_graph(gp_attn, args.kernel_reps, 2) / pw.n_calls
+        fl = pw.flops_per_call()
+        tflops = fl / (ms_pa * 1e-3) / 1e12
+        result["prefill"] = {
+            "config": pw.describe(), "ms_per_step": round(ms_p, 4),
+            "tflops_step": round(fl * pw.n_calls / (ms_p * 1e-3) / 1e12, 2),
+            "roofline": dict(bound="mfma", achieved=round(tflops, 2),
+                             peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                             frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                             traffic=None, kernel="prefill attention",
+                             algorithmic_flops_per_call=fl, us_per_call=round(ms_pa * 1e3, 3)),
+            "prologue_bytes_per_call": pw.prologue_bytes(),
+        }
+        del gp_step, gp_attn
+
+    if not args.no_cpu_baseline:
+        log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s each)")
+        result["cpu_baseline"] = cpu_decode_baseline(args.cpu_seconds)
+        if "prefill" in result:
+            result["prefill"]["cpu_baseline"] = cpu_prefill_baseline(args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    result["host"] = dict(cpu_count=os.cpu_count(),
+                          affinity=len(os.sched_getaffinity(0)),
+                          device=torch.cuda.get_device_name(0))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

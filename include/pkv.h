@@ -121,7 +121,8 @@ pkv_status pkv_append(const void* k_new, const void* v_new, const int32_t* slot,
                       const pkv_cache_desc* cd, void* k_pool, void* v_pool, void* stream);
 
 /* ---------------------------------------------------------------------------
- * pkv_attn_decode -- one query token per batch row against its slot's pages.
+ * pkv_attn_decode -- one query token per batch row against its slot's pages,
+ * optionally appending that token's K/V first (fused append).
  * Masks: the query sits at position L-1 (L = seq_lens[b], the key count after
  * the append) and sees key j iff j <= L-1 and, with window W > 0, L-1-j < W
  * ([continuous-batching compare] flex_paged_attention.py,
@@ -131,24 +132,31 @@ pkv_status pkv_append(const void* k_new, const void* v_new, const int32_t* slot,
  *   q        : device bf16 [B][n_q_heads][head_dim]
  *   slots    : device int32 [B]; seq_lens: device int32 [B]
  *              rows with slot 0 or seq_len 0 are idle: out = 0, lse = -inf,
- *              nothing read ([continuous-batching compare] results write-up:
- *              padded rows must come out as zeros, not NaN)
+ *              nothing read or written ([continuous-batching compare] results
+ *              write-up: padded rows must come out as zeros, not NaN)
  *   max_seq_len_hint : host int >= 1, an upper bound of seq_lens used to size
  *              the split-K grid (results stay correct if exceeded; only speed
  *              changes)
+ *   k_pool, v_pool : device pools; written only when k_new / v_new are given
+ *   k_new, v_new : device bf16 [B][n_kv_heads][head_dim] or both NULL.  When
+ *              given, each active row's new token is first written at position
+ *              L-1 of its slot, exactly as pkv_append would (the decode form of
+ *              PageTable.assign), and then attended.
  *   scale    : softmax scale applied to q.k (e.g. 1/sqrt(head_dim))
  *   window   : 0 = full causal, W > 0 = sliding window of W keys incl. self
  *   out      : device bf16 [B][n_q_heads][head_dim]
  *   lse      : device fp32 [B][n_q_heads] natural-log sum-exp, or NULL
  *   workspace: device scratch of >= pkv_decode_workspace_size(...) bytes
- *              (NULL allowed when that size is 0); contents need no init.
+ *              (NULL allowed when that size is 0); its contents need no
+ *              initialisation.  Calls that share a workspace must not run
+ *              concurrently.
  * n_q_heads / n_kv_heads must be an integer G in [1, 16] with G * head_dim <= 2048
  * (PKV_ERR_UNSUPPORTED otherwise).  B == 0 is a no-op.
  */
 pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slots,
                            const int32_t* seq_lens, int32_t B, int32_t max_seq_len_hint,
-                           pkv_page_table pt, const pkv_cache_desc* cd,
-                           const void* k_pool, const void* v_pool, float scale,
+                           pkv_page_table pt, const pkv_cache_desc* cd, void* k_pool,
+                           void* v_pool, const void* k_new, const void* v_new, float scale,
                            int32_t window, void* out, float* lse, void* workspace,
                            size_t workspace_bytes, void* stream);
 

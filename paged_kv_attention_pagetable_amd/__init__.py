@@ -24,7 +24,7 @@ from . import _lib
 from ._lib import CacheDesc, PageTableRef, Prologue, PkvError, check, lib
 
 __all__ = ["append", "attn_decode", "attn_prefill", "decode_workspace_size", "rope_table",
-           "new_pools", "PageAllocator", "PkvError", "lib"]
+           "new_pools", "new_decode_workspace", "PageAllocator", "PkvError", "lib"]
 
 
 def _ptr(t):
@@ -101,8 +101,13 @@ def decode_workspace_size(B, n_q, n_kv, head_dim, max_seq_len_hint, window=0):
 
 
 def attn_decode(q, slots, seq_lens, table, k_pool, v_pool, scale=None, window=0,
-                max_seq_len_hint=None, out=None, lse=None, workspace=None, stream=None):
-    """Decode attention; returns ``out [B, n_q, D]`` (bf16)."""
+                max_seq_len_hint=None, out=None, lse=None, workspace=None, k_new=None,
+                v_new=None, stream=None):
+    """Decode attention; returns ``out [B, n_q, D]`` (bf16).
+
+    With ``k_new``/``v_new`` ``[B, n_kv, D]`` each active row's new token is
+    appended at position ``seq_len - 1`` first (fused append).
+    """
     cd, pt = _cache(k_pool, v_pool, table)
     _bits16(q, "q")
     _i32(slots, "slots")
@@ -110,6 +115,13 @@ def attn_decode(q, slots, seq_lens, table, k_pool, v_pool, scale=None, window=0,
     B, n_q, D = q.shape
     if D != cd.head_dim:
         raise ValueError("q head_dim does not match the pools")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        _bits16(k_new, "k_new")
+        _bits16(v_new, "v_new")
+        if tuple(k_new.shape) != (B, cd.n_kv_heads, D) or v_new.shape != k_new.shape:
+            raise ValueError("k_new / v_new must be [B, n_kv, head_dim]")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if max_seq_len_hint is None:
@@ -118,13 +130,19 @@ def attn_decode(q, slots, seq_lens, table, k_pool, v_pool, scale=None, window=0,
         out = torch.empty((B, n_q, D), dtype=torch.bfloat16, device=q.device)
     ws_bytes = decode_workspace_size(B, n_q, cd.n_kv_heads, D, max_seq_len_hint, window)
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        workspace = new_decode_workspace(ws_bytes, q.device)
     wsize = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(lib().pkv_attn_decode(_ptr(q), n_q, _ptr(slots), _ptr(seq_lens), B,
                                 int(max_seq_len_hint), pt, ctypes.byref(cd), _ptr(k_pool),
-                                _ptr(v_pool), float(scale), int(window), _ptr(out), _ptr(lse),
-                                _ptr(workspace), wsize, _stream(stream, q.device)))
+                                _ptr(v_pool), _ptr(k_new), _ptr(v_new), float(scale),
+                                int(window), _ptr(out), _ptr(lse), _ptr(workspace), wsize,
+                                _stream(stream, q.device)))
     return out
+
+
+def new_decode_workspace(nbytes, device="cuda"):
+    """A decode workspace of ``nbytes`` (contents need no initialisation)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 def rope_table(max_pos, head_dim, theta, device="cuda", stream=None):

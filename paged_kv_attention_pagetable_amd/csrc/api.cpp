@@ -123,8 +123,8 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t n_q_heads, int32_t n_kv_head
 
 pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slots,
                            const int32_t* seq_lens, int32_t B, int32_t max_seq_len_hint,
-                           pkv_page_table pt, const pkv_cache_desc* cd,
-                           const void* k_pool, const void* v_pool, float scale,
+                           pkv_page_table pt, const pkv_cache_desc* cd, void* k_pool,
+                           void* v_pool, const void* k_new, const void* v_new, float scale,
                            int32_t window, void* out, float* lse, void* workspace,
                            size_t workspace_bytes, void* stream) {
   const char* fn = "pkv_attn_decode";
@@ -148,6 +148,8 @@ pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slot
   if (B == 0) return PKV_OK;
   if (!q || !slots || !seq_lens || !k_pool || !v_pool || !out)
     return fail(PKV_ERR_INVALID_ARG, "%s: NULL tensor pointer", fn);
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "%s: k_new and v_new must both be given or both be NULL", fn);
   const pkv::DecodePlan plan =
       pkv::plan_decode(B, n_q_heads, g.n_kv, g.head_dim, max_seq_len_hint, window);
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
@@ -164,12 +166,16 @@ pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slot
   a.g = g;
   a.kpool = static_cast<const pkv::bf16_t*>(k_pool);
   a.vpool = static_cast<const pkv::bf16_t*>(v_pool);
+  a.kpool_w = static_cast<pkv::bf16_t*>(k_pool);
+  a.vpool_w = static_cast<pkv::bf16_t*>(v_pool);
+  a.k_new = static_cast<const pkv::bf16_t*>(k_new);
+  a.v_new = static_cast<const pkv::bf16_t*>(v_new);
   a.scale_log2 = scale * pkv::kLog2eHost;
   a.window = window;
   a.split_tokens = plan.split_tokens;
   a.max_splits = plan.max_splits;
   a.part_o = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
-  a.part_ml = plan.ws_bytes ? static_cast<float*>(workspace) + plan.part_o_floats : nullptr;
+  a.part_ml = plan.ws_bytes ? a.part_o + plan.part_o_floats : nullptr;
   a.out = static_cast<pkv::bf16_t*>(out);
   a.lse = lse;
   return launched(pkv::launch_decode(a, static_cast<hipStream_t>(stream)), fn);

@@ -49,14 +49,18 @@ struct DecodeArgs {
   PoolGeom g;
   const bf16_t* kpool;
   const bf16_t* vpool;
-  float scale_log2;  // softmax scale * log2(e)
+  bf16_t* kpool_w;       // same pools, written by the fused append
+  bf16_t* vpool_w;
+  const bf16_t* k_new;   // [B][n_kv][D] new token K, or null (no fused append)
+  const bf16_t* v_new;
+  float scale_log2;      // softmax scale * log2(e)
   int window;
-  int split_tokens;  // keys per split (multiple of 128)
-  int max_splits;    // grid extent; 1 = no workspace, write out directly
-  float* part_o;     // [B][n_kv][max_splits][G][D]
-  float* part_ml;    // [B][n_kv][max_splits][G][2]  (running max in log2 units, sum)
-  bf16_t* out;       // [B][n_q][D]
-  float* lse;        // [B][n_q] or null
+  int split_tokens;      // keys per split (multiple of 128)
+  int max_splits;        // grid extent; 1 = no workspace, write out directly
+  float* part_o;         // [B][n_kv][max_splits][G][D]
+  float* part_ml;        // [B][n_kv][max_splits][G][2]  (running max in log2 units, sum)
+  bf16_t* out;           // [B][n_q][D]
+  float* lse;            // [B][n_q] or null
 };
 
 struct PrologueArgs {
@@ -113,7 +117,7 @@ struct DecodePlan {
   int split_tokens;
   int max_splits;
   size_t ws_bytes;
-  size_t part_o_floats;  // offset of part_ml in floats
+  size_t part_o_floats;  // partial outputs first, then the (max, sum) pairs
 };
 DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_hint,
                        int window);

@@ -49,15 +49,16 @@ def gpu_pools(case):
     return kp, vp
 
 
-def gpu_decode_setup(case):
-    """Device pools with the history and the new token appended by the library."""
+def gpu_decode_setup(case, with_new_token=True):
+    """Device pools with the history (and the new token) appended by the library."""
     kp, vp = gpu_pools(case)
     table = dev_i32(case.table)
     hk, hv, hs, hp = case.history_tokens()
     if len(hs):
         pkv.append(dev_bits(hk), dev_bits(hv), dev_i32(hs), dev_i32(hp), table, kp, vp)
-    pkv.append(dev_bits(case.k_new), dev_bits(case.v_new), dev_i32(case.append_slots()),
-               dev_i32(case.append_pos()), table, kp, vp)
+    if with_new_token:
+        pkv.append(dev_bits(case.k_new), dev_bits(case.v_new), dev_i32(case.append_slots()),
+                   dev_i32(case.append_pos()), table, kp, vp)
     return kp, vp, table
 
 
@@ -70,11 +71,15 @@ def oracle_decode_pools(case):
     return kp, vp
 
 
-def run_gpu_decode(case, kp, vp, table, hint=None, with_lse=True):
+def run_gpu_decode(case, kp, vp, table, hint=None, with_lse=True, fused_append=False,
+                   workspace=None):
     q = dev_bits(case.q)
     lse = torch.empty((case.B, case.n_q), dtype=torch.float32, device=DEV) if with_lse else None
+    kn = dev_bits(case.k_new) if fused_append else None
+    vn = dev_bits(case.v_new) if fused_append else None
     out = pkv.attn_decode(q, dev_i32(case.slots), dev_i32(case.seq_lens), table, kp, vp,
                           scale=case.scale, window=case.window,
-                          max_seq_len_hint=hint or max(int(case.seq_lens.max()), 1), lse=lse)
+                          max_seq_len_hint=hint or max(int(case.seq_lens.max()), 1), lse=lse,
+                          k_new=kn, v_new=vn, workspace=workspace)
     torch.cuda.synchronize()
     return out, lse

@@ -44,8 +44,8 @@ def _decode(**kw):
     a = args
     return pkv.lib().pkv_attn_decode(a["q"], a["n_q"], a["slots"], a["seq_lens"], a["B"],
                                      a["hint"], a["pt"], ctypes.byref(a["cd"]), a["k"], a["v"],
-                                     a["scale"], a["window"], a["out"], a["lse"], a["ws"],
-                                     a["ws_bytes"], None)
+                                     a.get("k_new"), a.get("v_new"), a["scale"], a["window"],
+                                     a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
 
 
 def test_decode_argument_checks_return_before_launch():
@@ -61,6 +61,8 @@ def test_decode_argument_checks_return_before_launch():
     assert _decode(scale=float("nan")) == 1
     assert _decode(hint=0) == 1
     assert _decode(B=-1) == 1
+    assert _decode(k_new=1) == 1                     # k_new without v_new
+    assert _decode(n_q=2 * 16, cd=_desc(D=256)) == 2  # G * head_dim above 2048
     # a split-K plan needs a workspace
     need = pkv.decode_workspace_size(64, 32, 8, 128, 4096, 0)
     assert need > 0

@@ -51,6 +51,38 @@ def test_decode_matches_oracle(name):
     assert np.all(host_bits(out)[idle] == 0)
 
 
+@pytest.mark.parametrize("name", ["tiny", "d128_g4_edges", "d128_ps16", "d256_w512",
+                                  "d512_full"])
+def test_decode_fused_append_equals_append_then_decode(name):
+    n_q, n_kv, D, ps, lengths, window, scale = CASES[name]
+    case = make_decode_case(n_q, n_kv, D, ps, lengths, max_slots=len(lengths) + 2,
+                            seed=1500 + D, window=window, scale=scale, spare_pages=2)
+    kp, vp, table = gpu_decode_setup(case)
+    ref_out, ref_lse = run_gpu_decode(case, kp, vp, table)
+    kp2, vp2, table2 = gpu_decode_setup(case, with_new_token=False)
+    out, lse = run_gpu_decode(case, kp2, vp2, table2, fused_append=True)
+    okp, ovp = oracle_decode_pools(case)
+    assert np.array_equal(host_bits(kp2), okp), "fused append: K pool differs from the oracle"
+    assert np.array_equal(host_bits(vp2), ovp), "fused append: V pool differs from the oracle"
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    assert torch.equal(lse, ref_lse)
+
+
+def test_decode_workspace_reused_across_calls_and_shapes():
+    """One uninitialised workspace serves successive calls of different sizes."""
+    ws = pkv.new_decode_workspace(pkv.decode_workspace_size(64, 32, 8, 128, 4096), "cuda")
+    ws.fill_(0x7F)  # garbage: the partials must never be read before written
+    for seed, lengths in ((1, [4000, 17, 0, 2500, 999]), (2, [129, 3000]), (3, [4096] * 6)):
+        case = make_decode_case(32, 8, 128, 128, lengths, max_slots=len(lengths) + 1,
+                                seed=seed, spare_pages=1)
+        kp, vp, table = gpu_decode_setup(case)
+        out, _ = run_gpu_decode(case, kp, vp, table, hint=4096, workspace=ws)
+        okp, ovp = oracle_decode_pools(case)
+        ref, _ = oracle.attn_decode(case.q, okp, ovp, case.table, case.slots, case.seq_lens,
+                                    case.scale, 0)
+        assert_attn_close(host_f64(out), ref, f"reuse {seed}")
+
+
 def test_decode_length_one_returns_v_exactly():
     case = make_decode_case(8, 2, 128, 16, [1, 1, 1], max_slots=5, seed=3)
     kp, vp, table = gpu_decode_setup(case)
