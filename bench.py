@@ -273,6 +273,80 @@ def pmc_traffic(tag, sources, launches_per_call=1):
 
 
 # ----------------------------------------------------------------------------
+# rocprofv3 summaries (kernel durations, HBM counters)
+# ----------------------------------------------------------------------------
+
+def _kernel_rows(db_path):
+    import sqlite3
+    db = sqlite3.connect(db_path)
+    return db.execute("select name, duration from kernels").fetchall()
+
+
+def summarize_trace(db_path, out_path, command=""):
+    rows = _kernel_rows(db_path)
+    stats = {}
+    for name, dur in rows:
+        stats.setdefault(name, []).append(dur / 1e3)
+    lines = ["# rocprofv3 kernel trace summary", "",
+             f"Command: `{command}`" if command else "", "",
+             "| kernel | dispatches | avg us | min us | max us | total us |",
+             "|---|---|---|---|---|---|"]
+    for name, d in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        if "pkv::" not in name and "copy" not in name:
+            continue
+        short = name.replace("void ", "").replace("pkv::(anonymous namespace)::", "").split("(")[0]
+        lines.append(f"| {short} | {len(d)} | {np.mean(d):.3f} | {np.min(d):.3f} | "
+                     f"{np.max(d):.3f} | {np.sum(d):.1f} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _pmc_per_kernel(db_path, counter):
+    """Counter values per dispatch, grouped by kernel name."""
+    import sqlite3
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select name, dispatch_id, sum(counter_value) from pmc_events "
+                      "where counter_name = ? group by dispatch_id", (counter,)).fetchall()
+    acc = {}
+    for name, _, v in rows:
+        acc.setdefault(name, []).append(v)
+    return acc
+
+
+def summarize_pmc(fetch_db, write_db, out_prefix, workload="qwen3_decode", command=""):
+    """HBM bytes per decode call = (split + merge) FETCH_SIZE + WRITE_SIZE (KiB per
+    dispatch), each scaled by what the counter reads for a 256 MiB device copy."""
+    fetch = _pmc_per_kernel(fetch_db, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_db, "WRITE_SIZE")
+    copy_bytes = 128 * 2**20 * 2
+
+    def copy_scale(tab):
+        vals = [v for k, vs in tab.items() if "copyBuffer" in k for v in vs]
+        return copy_bytes / (max(vals) * 1024.0) if vals else None
+
+    f_scale, w_scale = copy_scale(fetch), copy_scale(write)
+    per_call = 0.0
+    parts = {}
+    for k in sorted(set(fetch) | set(write)):
+        if "pkv::" not in k or "decode_" not in k:
+            continue
+        fb = float(np.mean(fetch.get(k, [0.0]))) * 1024.0 * (f_scale or 1.0)
+        wb = float(np.mean(write.get(k, [0.0]))) * 1024.0 * (w_scale or 1.0)
+        per_call += fb + wb
+        short = k.replace("void ", "").replace("pkv::(anonymous namespace)::", "").split("(")[0]
+        parts[short] = dict(fetch_bytes=round(fb), write_bytes=round(wb),
+                            dispatches=len(fetch.get(k, [])))
+    sources = ["decode.hip", "pkv_device.h", "pkv_internal.h"]
+    rec = dict(workload=workload, source_sha=source_sha(sources),
+               hbm_bytes_per_call=round(per_call), kernels=parts,
+               copy_scale=dict(fetch=f_scale, write=w_scale, copy_bytes=copy_bytes),
+               command=command)
+    with open(out_prefix + ".json", "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+# ----------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample)
 # ----------------------------------------------------------------------------
 
@@ -375,7 +449,21 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel-reps", type=int, default=20,
                     help="replays of the attention-only graphs for kernel timing")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("DB", "OUT"),
+                    help="write a kernel-duration summary of a rocprofv3 database and exit")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "OUT"),
+                    help="write HBM traffic per decode call from two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--command", default="", help="command line recorded in summaries")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, command=args.command)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, workload=args.workload, command=args.command)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this bench runs the single-GPU path only; "
                                    f"--gpus {args.gpus} is not supported (use --gpus 1)"}))
@@ -405,7 +493,7 @@ def main():
     traffic = pmc_traffic(f"decode_{args.workload}", dec_sources)
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-                    kernel="decode attention (split-K + in-kernel LSE merge)",
+                    kernel="decode attention (split-K kernel + LSE merge kernel)",
                     algorithmic_bytes_per_call=int(sum(attn_bytes) / wl.n_calls),
                     us_per_call=round(ms_attn * 1e3, 3))
     result = {
@@ -416,6 +504,13 @@ def main():
         "config": wl.describe(), "roofline": roofline,
     }
     del g_step, g_attn
+    if args.calibrate_copy:
+        src = torch.empty(128 * 2**20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     if not args.no_prefill:
         log("setting up qwen3_prefill")

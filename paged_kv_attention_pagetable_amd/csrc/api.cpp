@@ -206,6 +206,9 @@ pkv_status pkv_attn_prefill(void* q, int32_t n_q_heads, const int32_t* cu_seqlen
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "%s: scale must be finite", fn);
   if (max_seqlen_q_hint < 1)
     return fail(PKV_ERR_INVALID_ARG, "%s: max_seqlen_q_hint must be >= 1", fn);
+  if (pt.pages_per_slot > 4096)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: pages_per_slot must be <= 4096 (got %d)", fn,
+                pt.pages_per_slot);
   if (n_seqs == 0 || total_tokens == 0) return PKV_OK;
   if (!q || !cu_seqlens || !slots || !k_pool || !v_pool || !out)
     return fail(PKV_ERR_INVALID_ARG, "%s: NULL tensor pointer", fn);
