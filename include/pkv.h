@@ -189,7 +189,7 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t n_q_heads, int32_t n_kv_head
  *   out        : device bf16 [total_tokens][n_q_heads][head_dim]
  *   lse        : device fp32 [total_tokens][n_q_heads] or NULL
  *   workspace  : unused by the current kernels (pass NULL / 0)
- * head_dim 512 and pages_per_slot > 4096 are not supported here
+ * head_dim 512 and pages_per_slot > 2048 are not supported here
  * (PKV_ERR_UNSUPPORTED).
  */
 pkv_status pkv_attn_prefill(void* q, int32_t n_q_heads, const int32_t* cu_seqlens,

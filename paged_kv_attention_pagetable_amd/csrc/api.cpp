@@ -174,6 +174,7 @@ pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slot
   a.window = window;
   a.split_tokens = plan.split_tokens;
   a.max_splits = plan.max_splits;
+  a.waves = plan.waves;
   a.part_o = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
   a.part_ml = plan.ws_bytes ? a.part_o + plan.part_o_floats : nullptr;
   a.out = static_cast<pkv::bf16_t*>(out);
@@ -206,8 +207,8 @@ pkv_status pkv_attn_prefill(void* q, int32_t n_q_heads, const int32_t* cu_seqlen
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "%s: scale must be finite", fn);
   if (max_seqlen_q_hint < 1)
     return fail(PKV_ERR_INVALID_ARG, "%s: max_seqlen_q_hint must be >= 1", fn);
-  if (pt.pages_per_slot > 4096)
-    return fail(PKV_ERR_UNSUPPORTED, "%s: pages_per_slot must be <= 4096 (got %d)", fn,
+  if (pt.pages_per_slot > 2048)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: pages_per_slot must be <= 2048 (got %d)", fn,
                 pt.pages_per_slot);
   if (n_seqs == 0 || total_tokens == 0) return PKV_OK;
   if (!q || !cu_seqlens || !slots || !k_pool || !v_pool || !out)

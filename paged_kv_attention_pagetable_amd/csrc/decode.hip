@@ -87,15 +87,15 @@ __device__ __forceinline__ void append_new_token(const DecodeArgs& a, const RowR
   const size_t dst = (size_t)page * a.g.n_kv * blk + hk * blk;
   const int row = p & (ps - 1);
   const size_t src = ((size_t)b * a.g.n_kv + hk) * D;
-  for (int i = threadIdx.x; i < D / 8; i += kThreads)
+  for (int i = threadIdx.x; i < D / 8; i += blockDim.x)
     store16(a.kpool_w + dst + (size_t)row * D + 8 * i, load16(a.k_new + src + 8 * i));
-  for (int d = threadIdx.x; d < D; d += kThreads) a.vpool_w[dst + (size_t)d * ps + row] = a.v_new[src + d];
+  for (int d = threadIdx.x; d < D; d += blockDim.x) a.vpool_w[dst + (size_t)d * ps + row] = a.v_new[src + d];
 }
 
 // Stages the page ids of logical pages [p0, p0 + n) of the row into LDS.
 __device__ __forceinline__ void stage_pages(const DecodeArgs& a, const int32_t* trow, int p0, int n,
                                             int* s_pg) {
-  for (int i = threadIdx.x; i < n; i += kThreads) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const int pg = trow[p0 + i];
     s_pg[i] = (pg >= 1 && pg < a.g.n_pages) ? pg : -1;
   }
@@ -109,7 +109,7 @@ __device__ void finish(const DecodeArgs& a, int b, int hk, int s, OFn o_val, MFn
   const int G = a.G;
   const int tid = threadIdx.x;
   if (a.max_splits == 1) {
-    for (int idx = tid; idx < G * D; idx += kThreads) {
+    for (int idx = tid; idx < G * D; idx += blockDim.x) {
       const int g = idx / D, d = idx - g * D;
       const float l = Lof(g);
       a.out[((size_t)b * a.n_q + hk * G + g) * D + d] = f32_to_bf16(l > 0.f ? o_val(g, d) / l : 0.f);
@@ -119,11 +119,11 @@ __device__ void finish(const DecodeArgs& a, int b, int hk, int s, OFn o_val, MFn
     return;
   }
   const size_t pbase = ((size_t)b * a.g.n_kv + hk) * a.max_splits + s;
-  for (int idx = tid; idx < G * D; idx += kThreads) {
+  for (int idx = tid; idx < G * D; idx += blockDim.x) {
     const int g = idx / D, d = idx - g * D;
     a.part_o[(pbase * G + g) * D + d] = o_val(g, d);
   }
-  for (int g = tid; g < G; g += kThreads) {
+  for (int g = tid; g < G; g += blockDim.x) {
     a.part_ml[(pbase * G + g) * 2] = Mof(g);
     a.part_ml[(pbase * G + g) * 2 + 1] = Lof(g);
   }
@@ -134,7 +134,7 @@ __device__ void finish(const DecodeArgs& a, int b, int hk, int s, OFn o_val, MFn
 __device__ __forceinline__ void empty_partial(const DecodeArgs& a, int b, int hk, int s) {
   if (a.max_splits == 1) return;
   const size_t pbase = ((size_t)b * a.g.n_kv + hk) * a.max_splits + s;
-  for (int g = threadIdx.x; g < a.G; g += kThreads) {
+  for (int g = threadIdx.x; g < a.G; g += blockDim.x) {
     a.part_ml[(pbase * a.G + g) * 2] = -INFINITY;
     a.part_ml[(pbase * a.G + g) * 2 + 1] = 0.f;
   }
@@ -142,7 +142,7 @@ __device__ __forceinline__ void empty_partial(const DecodeArgs& a, int b, int hk
 
 __device__ __forceinline__ void idle_output(const DecodeArgs& a, int b, int hk, int s, int D) {
   if (a.max_splits == 1) {
-    for (int idx = threadIdx.x; idx < a.G * D; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < a.G * D; idx += blockDim.x) {
       const int g = idx / D, d = idx - g * D;
       a.out[((size_t)b * a.n_q + hk * a.G + g) * D + d] = 0;
       if (a.lse && d == 0) a.lse[(size_t)b * a.n_q + hk * a.G + g] = -INFINITY;
@@ -205,13 +205,13 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// head_dim <= 128: key split across the 4 waves.
-template <int D>
-__global__ __launch_bounds__(kThreads) void decode_keysplit_kernel(DecodeArgs a) {
+// head_dim <= 128: key split across the NW waves of the workgroup.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_keysplit_kernel(DecodeArgs a) {
+  extern __shared__ float s_o[];                  // [wave][G][D] (dynamic: NW * G * D)
   __shared__ int s_pg[kSegPages];
-  __shared__ float s_o[kDecodeWaves * kMaxGD];    // [wave][G][D], G * D <= kMaxGD
-  __shared__ float s_ml[2 * kDecodeWaves * 16];  // [wave][16] max, then sum
-  __shared__ float s_red[128];
+  __shared__ float s_ml[2 * NW * 16];             // [wave][16] max, then sum
+  __shared__ float s_red[NW * 16 + 32];
   const int s = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int qc = lane & 15, quad = lane >> 4;
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void decode_keysplit_kernel(DecodeArgs a)
         qreg[c] = qc < G ? v : u32x4{0, 0, 0, 0};
       }
     }
-    for (int t0 = seg0 + 32 * w; t0 < seg1; t0 += 32 * kDecodeWaves) {
+    for (int t0 = seg0 + 32 * w; t0 < seg1; t0 += 32 * NW) {
       // ---- issue the chunk's K and V^T loads together
       u32x4 kop[2][D / 32];
 #pragma unroll
@@ -329,34 +329,34 @@ __global__ __launch_bounds__(kThreads) void decode_keysplit_kernel(DecodeArgs a)
   }
   if (quad == 0) {
     s_ml[w * 16 + qc] = m_run;
-    s_ml[kDecodeWaves * 16 + w * 16 + qc] = l_run;
+    s_ml[NW * 16 + w * 16 + qc] = l_run;
   }
   __syncthreads();
   if (threadIdx.x < G) {
     const int g = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll
-    for (int w2 = 0; w2 < kDecodeWaves; ++w2) M = fmaxf(M, s_ml[w2 * 16 + g]);
+    for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, s_ml[w2 * 16 + g]);
     const float Mu = M == -INFINITY ? 0.f : M;
     float lsum = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < kDecodeWaves; ++w2) {
+    for (int w2 = 0; w2 < NW; ++w2) {
       const float f = fast_exp2(s_ml[w2 * 16 + g] - Mu);
       s_red[w2 * 16 + g] = f;
-      lsum += f * s_ml[kDecodeWaves * 16 + w2 * 16 + g];
+      lsum += f * s_ml[NW * 16 + w2 * 16 + g];
     }
-    s_red[64 + g] = M;
-    s_red[80 + g] = lsum;
+    s_red[NW * 16 + g] = M;
+    s_red[NW * 16 + 16 + g] = lsum;
   }
   __syncthreads();
   auto o_val = [&](int g, int d) {
     float o = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < kDecodeWaves; ++w2) o += s_red[w2 * 16 + g] * s_o[(w2 * G + g) * D + d];
+    for (int w2 = 0; w2 < NW; ++w2) o += s_red[w2 * 16 + g] * s_o[(w2 * G + g) * D + d];
     return o;
   };
-  auto Mof = [&](int g) { return s_red[64 + g]; };
-  auto Lof = [&](int g) { return s_red[80 + g]; };
+  auto Mof = [&](int g) { return s_red[NW * 16 + g]; };
+  auto Lof = [&](int g) { return s_red[NW * 16 + 16 + g]; };
   finish<D>(a, b, hk, s, o_val, Mof, Lof);
 }
 
@@ -502,9 +502,14 @@ __global__ __launch_bounds__(kThreads) void decode_dimsplit_kernel(DecodeArgs a)
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.max_splits, a.g.n_kv, a.B);
-  if constexpr (D <= 128)
-    hipLaunchKernelGGL((decode_keysplit_kernel<D>), grid, dim3(kThreads), 0, st, a);
-  else
+  if constexpr (D <= 128) {
+    if (a.waves == 8)
+      hipLaunchKernelGGL((decode_keysplit_kernel<D, 8>), grid, dim3(8 * 64),
+                         (size_t)8 * a.G * D * sizeof(float), st, a);
+    else
+      hipLaunchKernelGGL((decode_keysplit_kernel<D, kDecodeWaves>), grid, dim3(kThreads),
+                         (size_t)kDecodeWaves * a.G * D * sizeof(float), st, a);
+  } else
     hipLaunchKernelGGL((decode_dimsplit_kernel<D>), grid, dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;
@@ -533,6 +538,10 @@ DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_h
     split *= 2;
   p.split_tokens = (int)split;
   p.max_splits = (int)((range + split - 1) / split);
+  p.waves = kDecodeWaves;
+  // (One 8-wave workgroup per pair without a split was measured slower than
+  // split + merge even for 8 rows: 64 CUs stream ~16 GB/s each with
+  // sequential chunks.  The 8-wave variant stays available to the launcher.)
   if (p.max_splits <= 1) {
     p.max_splits = 1;
     p.ws_bytes = 0;

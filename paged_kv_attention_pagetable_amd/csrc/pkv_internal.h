@@ -57,6 +57,7 @@ struct DecodeArgs {
   int window;
   int split_tokens;      // keys per split (multiple of 128)
   int max_splits;        // grid extent; 1 = no workspace, write out directly
+  int waves;             // wave64s per workgroup of the split kernel (4 or 8)
   float* part_o;         // [B][n_kv][max_splits][G][D]
   float* part_ml;        // [B][n_kv][max_splits][G][2]  (running max in log2 units, sum)
   bf16_t* out;           // [B][n_q][D]
@@ -116,6 +117,7 @@ hipError_t launch_rope_table(float* c, float* s, int max_pos, int head_dim, doub
 struct DecodePlan {
   int split_tokens;
   int max_splits;
+  int waves;
   size_t ws_bytes;
   size_t part_o_floats;  // partial outputs first, then the (max, sum) pairs
 };

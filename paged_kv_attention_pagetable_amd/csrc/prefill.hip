@@ -3,23 +3,34 @@
 // Work item = (kv head, sequence, block of query tokens).  The G query heads
 // of the kv head are packed with the block's tokens into the MFMA column
 // dimension (column = token * G + head), so each K/V tile serves all of them.
-// A workgroup is 4 wave64s, each owning NT 16-column tiles.  Keys advance in
-// 64-key chunks.  Each chunk's K rows and V^T rows are gathered from their
-// physical pages (page ids staged in LDS once per workgroup) with 16-byte
-// loads; the next chunk's loads are in flight in registers while the current
-// chunk is computed from a double-buffered LDS tile, with one barrier per
-// chunk.  Per 32-key half and column tile every wave computes
+// A workgroup is 4 wave64s, each owning NT 16-column tiles (32 query columns
+// per wave at head_dim <= 128).  Registers are capped so that two waves run
+// per SIMD (two workgroups per CU): one wave's softmax overlaps the other's
+// MFMAs.  (64 columns per wave halve the LDS operand traffic but need ~350
+// registers, one wave per SIMD, and then the softmax serialises with the
+// MFMAs -- measured slower.)
+//
+// Keys advance in 64-key chunks.  Each chunk's K rows and V^T rows are copied
+// from their physical pages straight into LDS with gfx950's global-to-LDS
+// loads (16 bytes per lane, no staging registers); the next chunk's copies are
+// in flight while the current chunk is computed from the other LDS buffer,
+// with one wait + barrier per chunk.  Tiles are XOR-swizzled in 16-byte units
+// so that the MFMA operand reads of 16 rows hit 16 distinct bank groups.
+// Page ids of the workgroup's key range are staged in LDS once.
+//
+// Per 32-key half and column tile every wave computes
 //
 //   S^T[32 keys][16 cols] = K[32][D] . Q^T[D][16]
 //   O^T[D][16 cols]      += V^T[D][32] . P^T[32][16]
 //
 // with the same operand layout as the decode kernel (a lane's 8 key scores
-// are directly its P^T k-slots); the online softmax max/sum is updated once
-// per 64 keys.  Chunks entirely above a wave's causal diagonal, or entirely
-// left of its sliding window, are skipped without MFMA work; chunks entirely
-// visible skip the per-element mask.  Query blocks are issued longest-first,
-// and the workgroups of one (sequence, kv head) share an XCD L2 when the kv
-// head count is a multiple of 8 (grid x = kv head).
+// are directly its P^T k-slots).  The softmax keeps a reference max that only
+// moves when the running max outgrows it by 2^8, so the O accumulators are
+// rarely rescaled.  Chunks entirely above a wave's causal diagonal, or
+// entirely left of its sliding window, are skipped without MFMA work; chunks
+// entirely visible skip the per-element mask.  Query blocks are issued
+// longest-first, and the workgroups of one (sequence, kv head) share an XCD L2
+// when the kv head count is a multiple of 8 (grid x = kv head).
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -30,22 +41,35 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kChunk = 64;         // keys per pipeline step
-constexpr int kStagePages = 4096;  // page ids staged in LDS (>= pages_per_slot, host-checked)
+constexpr int kStagePages = 2048;  // page ids staged in LDS (>= pages_per_slot, host-checked)
 
+// 16-column MFMA tiles per wave.
 template <int D>
 constexpr int prefill_nt() { return D <= 128 ? 2 : 1; }
 
 template <int D>
-constexpr int k_row() { return D + 8; }         // bf16 elements per LDS K row (+16 B pad)
-constexpr int kVRow = kChunk + 8;               // bf16 elements per LDS V^T row (+16 B pad)
+constexpr int k_tile_bytes() { return kChunk * D * 2; }   // [64 keys][D] bf16
 template <int D>
-constexpr int tile_elems() { return kChunk * k_row<D>() + D * kVRow; }
+constexpr int tile_bytes() { return 2 * k_tile_bytes<D>(); }  // + V^T [D][64 keys]
 template <int D>
-constexpr int pieces() { return D / 32; }       // 16-byte pieces per thread per tile (K and V each)
+constexpr int dma_per_wave() { return D / 32; }  // 1 KB copies per wave, for K and for V each
+
+// Swizzles (16-byte slot of a row).  K row r holds chunk c (dims 8c..8c+7) at
+// slot c ^ k_swz(r); V^T row d holds key group g (keys 8g..8g+7) at slot
+// g ^ v_swz(d).  Both are bijections within a row; for the 16 rows one MFMA
+// operand read touches they give 16 distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  return D == 64 ? (((r >> 1) + 2 * (r >> 4)) & 7) : ((r + 4 * (r >> 4)) & 15);
+}
+__device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 template <int D, int NT>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
-  extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(PrefillArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int s_pg[kStagePages];
   const int hk = blockIdx.x, n = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -118,166 +142,166 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       s_pg[i] = (pg >= 1 && pg < n_pages) ? pg : -1;
     }
     __syncthreads();
-    // ---- per-thread prefetch of one chunk: K and V^T pieces.  Nothing here
-    // reads the loaded registers, so the loads stay in flight during the math.
-    u32x4 pk[pieces<D>()], pv[pieces<D>()];
-    auto fetch = [&](int j0) {
-      const bool tail = j0 + kChunk > kv_hi;  // uniform: only the last chunk is partial
+
+    // Copies the chunk at j0 into LDS buffer buf: this wave's share of the K
+    // and V^T 1 KB blocks.  Keys past kv_hi (and unmapped pages) read page 0
+    // so every address stays inside the pool; the scores of such keys are
+    // masked and their V^T entries zeroed after the copy lands.
+    auto issue = [&](int buf, int j0) {
+      uint8_t* tK = lds + buf * tile_bytes<D>();
+      uint8_t* tV = tK + k_tile_bytes<D>();
 #pragma unroll
-      for (int p = 0; p < pieces<D>(); ++p) {
-        const int i = tid + kThreads * p;
-        const int r = i / (D / 8), c8 = i - r * (D / 8);
+      for (int k = 0; k < dma_per_wave<D>(); ++k) {
+        const int m = w * dma_per_wave<D>() + k;
+        const int o = m * 1024 + 16 * lane;
+        const int r = o / (2 * D), s = (o % (2 * D)) >> 4;
+        const int c = s ^ k_swz<D>(r);
         const int j = j0 + r;
-        const int page = (!tail || j < kv_hi) ? s_pg[(j >> log2ps) - pg0] : -1;
-        pk[p] = page >= 0 ? load16(kbase + (size_t)page * page_stride + (size_t)(j & (ps - 1)) * D + 8 * c8)
-                          : u32x4{0, 0, 0, 0};
+        int page = j < kv_hi ? s_pg[(j >> log2ps) - pg0] : 0;
+        page = max(page, 0);
+        const bf16_t* src = kbase + (size_t)page * page_stride + (size_t)(j & (ps - 1)) * D + 8 * c;
+        __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(tK + m * 1024), 16, 0, 0);
       }
 #pragma unroll
-      for (int p = 0; p < pieces<D>(); ++p) {
-        const int i = tid + kThreads * p;
-        const int d = i >> 3, tg = i & 7;
-        const int j = j0 + 8 * tg;
-        const int page = (!tail || j < kv_hi) ? s_pg[(j >> log2ps) - pg0] : -1;
-        pv[p] = page >= 0 ? load16(vbase + (size_t)page * page_stride + (size_t)d * ps + (j & (ps - 1)))
-                          : u32x4{0, 0, 0, 0};
+      for (int k = 0; k < dma_per_wave<D>(); ++k) {
+        const int m = w * dma_per_wave<D>() + k;
+        const int o = m * 1024 + 16 * lane;
+        const int d = o >> 7, s = (o >> 4) & 7;
+        const int g = s ^ v_swz(d);
+        const int j = j0 + 8 * g;
+        int page = j < kv_hi ? s_pg[(j >> log2ps) - pg0] : 0;
+        page = max(page, 0);
+        const bf16_t* src = vbase + (size_t)page * page_stride + (size_t)d * ps + (j & (ps - 1));
+        __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(tV + m * 1024), 16, 0, 0);
       }
     };
-    // Writes the prefetched chunk at j0 to LDS buffer buf; V^T elements of keys
-    // at or beyond kv_hi are zeroed here (stale page rows may hold anything,
-    // and 0 * NaN would poison the P.V sum).
-    auto stash = [&](int buf, int j0) {
-      bf16_t* sK = lds + buf * tile_elems<D>();
-      bf16_t* sV = sK + kChunk * k_row<D>();
+    // After a tail chunk lands: zero the V^T entries of keys >= kv_hi (stale
+    // page rows may hold anything, and 0 * NaN would poison P.V).
+    auto zero_tail = [&](int buf, int j0) {
+      const int nvk = kv_hi - j0;
+      if (nvk >= kChunk) return;
+      uint8_t* tV = lds + buf * tile_bytes<D>() + k_tile_bytes<D>();
+      for (int idx = tid; idx < D * 8; idx += kThreads) {
+        const int d = idx >> 3, s = idx & 7;
+        const int g = s ^ v_swz(d);
+        const int nv = nvk - 8 * g;
+        if (nv >= 8) continue;
+        u32x4* p = reinterpret_cast<u32x4*>(tV + d * 128 + 16 * s);
+        u32x4 v = *p;
 #pragma unroll
-      for (int p = 0; p < pieces<D>(); ++p) {
-        const int i = tid + kThreads * p;
-        const int r = i / (D / 8), c8 = i - r * (D / 8);
-        store16(sK + r * k_row<D>() + 8 * c8, pk[p]);
-      }
-      const bool tail = j0 + kChunk > kv_hi;
-#pragma unroll
-      for (int p = 0; p < pieces<D>(); ++p) {
-        const int i = tid + kThreads * p;
-        const int d = i >> 3, tg = i & 7;
-        u32x4 v = pv[p];
-        if (tail) {
-          const int nv = kv_hi - (j0 + 8 * tg);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t m = (2 * e < nv ? 0x0000ffffu : 0u) | (2 * e + 1 < nv ? 0xffff0000u : 0u);
-            v[e] &= m;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t m = (2 * e < nv ? 0x0000ffffu : 0u) | (2 * e + 1 < nv ? 0xffff0000u : 0u);
+          v[e] &= m;
         }
-        store16(sV + d * kVRow + 8 * tg, v);
+        *p = v;
       }
     };
 
-    if (n_chunks > 0) {
-      fetch(j_start);
-      stash(0, j_start);
-    }
+    if (n_chunks > 0) issue(0, j_start);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
     __syncthreads();
+    if (n_chunks > 0 && j_start + kChunk > kv_hi) {
+      zero_tail(0, j_start);
+      __syncthreads();
+    }
     for (int ck = 0; ck < n_chunks; ++ck) {
       const int j0 = j_start + ck * kChunk;
-      if (ck + 1 < n_chunks) fetch(j0 + kChunk);  // in flight during this chunk's math
-      const bf16_t* sK = lds + (ck & 1) * tile_elems<D>();
-      const bf16_t* sV = sK + kChunk * k_row<D>();
+      if (ck + 1 < n_chunks) issue((ck + 1) & 1, j0 + kChunk);  // lands during this chunk's math
+      const uint8_t* tK = lds + (ck & 1) * tile_bytes<D>();
+      const uint8_t* tV = tK + k_tile_bytes<D>();
       const bool skip = wave_hi < 0 || j0 > wave_hi ||
                         (a.window > 0 && j0 + kChunk - 1 <= wave_lo - a.window);
       if (!skip) {
         const bool full = (j0 + kChunk - 1 <= wave_lo) && (a.window <= 0 || wave_hi - j0 < a.window);
-        // ---- S^T = K Q^T: half h, MFMA rg rows m hold keys 32h + 8*(m/4) + 4*rg + m%4
-        f32x4 S[NT][2][2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
+#pragma unroll 1
+        for (int h = 0; h < 2; ++h) {
+          // ---- S^T = K Q^T for keys j0 + 32h + ..: MFMA rg row m holds key 8*(m/4) + 4*rg + m%4
+          f32x4 S[NT][2];
 #pragma unroll
           for (int rg = 0; rg < 2; ++rg) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) S[nt][h][rg] = f32x4{0.f, 0.f, 0.f, 0.f};
             const int r = 32 * h + 8 * (qc >> 2) + 4 * rg + (qc & 3);
-            const bf16_t* kr = sK + r * k_row<D>() + 8 * quad;
+            const uint8_t* kr = tK + r * (2 * D);
+            const int sw = k_swz<D>(r);
+            {
+              const u32x4 kv = *reinterpret_cast<const u32x4*>(kr + 16 * (quad ^ sw));
 #pragma unroll
-            for (int c = 0; c < D / 32; ++c) {
-              const u32x4 kv = load16(kr + 32 * c);
+              for (int nt = 0; nt < NT; ++nt)
+                S[nt][rg] = mfma16x16x32(kv, qreg[nt][0], f32x4{0.f, 0.f, 0.f, 0.f});
+            }
 #pragma unroll
-              for (int nt = 0; nt < NT; ++nt) S[nt][h][rg] = mfma16x16x32(kv, qreg[nt][c], S[nt][h][rg]);
+            for (int c = 1; c < D / 32; ++c) {
+              const u32x4 kv = *reinterpret_cast<const u32x4*>(kr + 16 * ((4 * c + quad) ^ sw));
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) S[nt][rg] = mfma16x16x32(kv, qreg[nt][c], S[nt][rg]);
             }
           }
-        // ---- scores in log2 units; lane holds keys j0 + 32h + 8*quad + jj
-        float sc[NT][2][8];
+          // ---- element mask, only on chunks crossing the diagonal or the window edge
+          if (!full) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+            for (int nt = 0; nt < NT; ++nt) {
+              const int pc = pcol[nt];
+              const int jmin = a.window > 0 ? pc - a.window + 1 : -0x7fffffff;
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+              for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
-              sc[nt][h][jj] = (jj < 4 ? S[nt][h][0][jj] : S[nt][h][1][jj - 4]) * a.scale_log2;
-        if (!full) {  // wave-uniform: only chunks crossing the diagonal or the window edge
+                for (int e = 0; e < 4; ++e) {
+                  const int j = j0 + 32 * h + 8 * quad + 4 * rg + e;
+                  if (j > pc || j < jmin) S[nt][rg][e] = -INFINITY;
+                }
+            }
+          }
+          // ---- online softmax with a lazily moved reference max: p = 2^(s*c - m_ref)
+          // stays exact; m_ref only moves (and O is rescaled) when the running
+          // max exceeds it by more than 2^8, so p <= 256 and rescales are rare.
+          u32x4 pb[NT];
+          float alpha[NT];
+          bool resc = false;
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
-            const int pc = pcol[nt];
-            const int jmin = a.window > 0 ? pc - a.window + 1 : -0x7fffffff;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-              for (int jj = 0; jj < 8; ++jj) {
-                const int j = j0 + 32 * h + 8 * quad + jj;
-                if (j > pc || j < jmin) sc[nt][h][jj] = -INFINITY;
-              }
-          }
-        }
-        // ---- online softmax over the 64 keys, per column tile
-        u32x4 pb[NT][2];
-        float alpha[NT];
-        bool rescale = false;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) mx = fmaxf(mx, sc[nt][h][jj]);
-          mx = fmaxf(mx, shfl_xor(mx, 16));
-          mx = fmaxf(mx, shfl_xor(mx, 32));
-          const float m_new = fmaxf(m_run[nt], mx);
-          const float m_use = m_new == -INFINITY ? 0.f : m_new;
-          alpha[nt] = fast_exp2(m_run[nt] - m_use);
-          rescale |= m_new != m_run[nt];
-          float psum = 0.f;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
+            float mx = fmaxf(fmaxf(fmaxf(S[nt][0][0], S[nt][0][1]), fmaxf(S[nt][0][2], S[nt][0][3])),
+                             fmaxf(fmaxf(S[nt][1][0], S[nt][1][1]), fmaxf(S[nt][1][2], S[nt][1][3])));
+            mx = fmaxf(mx, shfl_xor(mx, 16));
+            mx = fmaxf(mx, shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run[nt], mx * a.scale_log2);
+            const bool need = m_new > m_run[nt] + 8.0f;
+            alpha[nt] = need ? fast_exp2(m_run[nt] - m_new) : 1.0f;
+            if (need) m_run[nt] = m_new;
+            resc |= need;
+            const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
             float p[8];
+            float psum = 0.f;
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-              p[jj] = fast_exp2(sc[nt][h][jj] - m_use);
-              psum += p[jj];
+            for (int e = 0; e < 8; ++e) {
+              p[e] = fast_exp2(fmaf(S[nt][e >> 2][e & 3], a.scale_log2, -m_use));
+              psum += p[e];
             }
-            pb[nt][h] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                              pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+            l_run[nt] = l_run[nt] * alpha[nt] + psum;
+            pb[nt] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
           }
-          l_run[nt] = l_run[nt] * alpha[nt] + psum;
-          m_run[nt] = m_new;
-        }
-        // The O accumulators only need rescaling when some column's max moved
-        // (alpha is exactly 1 otherwise); that is rare after the first chunks.
-        if (__any(rescale)) {
+          if (__any(resc)) {
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) acc[nt][dt] *= alpha[nt];
-        }
-        // ---- O^T += V^T P^T over both halves
+              for (int dt = 0; dt < D / 16; ++dt) acc[nt][dt] *= alpha[nt];
+          }
+          // ---- O^T += V^T P^T for this half; lane row d = 16*dt + qc, keys group 4h + quad
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const u32x4 v0 = load16(sV + (16 * dt + qc) * kVRow + 8 * quad);
-          const u32x4 v1 = load16(sV + (16 * dt + qc) * kVRow + 32 + 8 * quad);
+          for (int dt = 0; dt < D / 16; ++dt) {
+            const int d = 16 * dt + qc;
+            const u32x4 vv =
+                *reinterpret_cast<const u32x4*>(tV + d * 128 + 16 * ((4 * h + quad) ^ v_swz(d)));
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            acc[nt][dt] = mfma16x16x32(v1, pb[nt][1], mfma16x16x32(v0, pb[nt][0], acc[nt][dt]));
+            for (int nt = 0; nt < NT; ++nt) acc[nt][dt] = mfma16x16x32(vv, pb[nt], acc[nt][dt]);
+          }
         }
       }
-      if (ck + 1 < n_chunks) stash((ck + 1) & 1, j0 + kChunk);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk's copies have landed
       __syncthreads();
+      if (ck + 1 < n_chunks && j0 + 2 * kChunk > kv_hi) {
+        zero_tail((ck + 1) & 1, j0 + kChunk);
+        __syncthreads();
+      }
     }
 
     // ---- normalise and store
@@ -309,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 template <int D>
 hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t st) {
   constexpr int NT = prefill_nt<D>();
-  const size_t lds = 2 * (size_t)tile_elems<D>() * sizeof(bf16_t);
+  const size_t lds = 2 * (size_t)tile_bytes<D>();
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&prefill_kernel<D, NT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
