@@ -187,6 +187,7 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t n_q_heads, int32_t n_kv_head
  *   max_seqlen_q_hint : host int >= 1, bound of the per-sequence token counts
  *                used for grid sizing (correct if exceeded; only speed changes)
  *   out        : device bf16 [total_tokens][n_q_heads][head_dim]
+ *   scale      : softmax scale applied to q.k, finite and > 0
  *   lse        : device fp32 [total_tokens][n_q_heads] or NULL
  *   workspace  : unused by the current kernels (pass NULL / 0)
  * head_dim 512 and pages_per_slot > 2048 are not supported here

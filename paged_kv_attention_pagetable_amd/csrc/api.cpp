@@ -204,7 +204,8 @@ pkv_status pkv_attn_prefill(void* q, int32_t n_q_heads, const int32_t* cu_seqlen
   st = check_heads(fn, n_q_heads, g.n_kv, &G);
   if (st != PKV_OK) return st;
   if (window < 0) return fail(PKV_ERR_INVALID_ARG, "%s: window must be >= 0", fn);
-  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(PKV_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
   if (max_seqlen_q_hint < 1)
     return fail(PKV_ERR_INVALID_ARG, "%s: max_seqlen_q_hint must be >= 1", fn);
   if (pt.pages_per_slot > 2048)

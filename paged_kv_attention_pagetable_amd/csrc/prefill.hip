@@ -66,6 +66,28 @@ __device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Max of the 8 scores a lane holds for its column (two 4-row accumulators).
+// Scores are finite or -inf (masked), so the NaN-propagating maximum needs no
+// canonicalisation of the MFMA results.
+__device__ __forceinline__ float max8(const f32x4 (&s)[2]) {
+  return vmax(vmax(vmax(s[0][0], s[0][1]), vmax(s[0][2], s[0][3])),
+              vmax(vmax(s[1][0], s[1][1]), vmax(s[1][2], s[1][3])));
+}
+
+// Max over the four lanes l, l^16, l^32, l^48 (the 4 key groups of a column)
+// with gfx950's row-swap permutes: each swap hands every lane its partner's
+// value in one of the two outputs.
+__device__ __forceinline__ float quad_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = vmax(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+  const uint32_t w = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return vmax(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+}
+
 template <int D, int NT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
@@ -88,6 +110,35 @@ void prefill_kernel(PrefillArgs a) {
   const bf16_t* vbase = a.vpool + hk * blk;
   const int32_t* trow = a.pt.table + (size_t)(idle ? 0 : slot) * a.pt.pps;
   const int cap = a.pt.pps * ps;
+  const float inv_c = 1.0f / a.scale_log2;  // scale > 0 (host-checked)
+  // LDS byte offsets (within a tile buffer) of this lane's MFMA operand rows.
+  // K row r, dims chunk c sits at kofs ^ (64 * c): the row's swizzle is folded
+  // into kofs and 64*c only flips bits inside the row.  V^T rows d = 16*dt + qc
+  // share one swizzle across dt, so dt is a plain 2 KB step from vofs.
+  int kofs[2][2], vofs[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      const int r = 32 * h + 8 * (qc >> 2) + 4 * rg + (qc & 3);
+      kofs[h][rg] = r * (2 * D) + 16 * (quad ^ k_swz<D>(r));
+    }
+    vofs[h] = k_tile_bytes<D>() + qc * 128 + 16 * ((4 * h + quad) ^ v_swz(qc));
+  }
+  // Source byte offsets of this lane's tile copies, relative to the chunk's
+  // first key in its page.  Copy k of the wave fills tile bytes m*1024 ..
+  // m*1024+1023 (m = w*dpw + k), lane i the 16 bytes at +16*i.  K: tile row r
+  // slot s holds dims 8*(s ^ k_swz(r)) ..  V^T: row d slot s holds keys
+  // 8*(s ^ v_swz(d)) .. (V pages are d-major: element (d, key) at d*ps + key).
+  uint32_t dma_k[dma_per_wave<D>()], dma_v[dma_per_wave<D>()];
+#pragma unroll
+  for (int k = 0; k < dma_per_wave<D>(); ++k) {
+    const int o = (w * dma_per_wave<D>() + k) * 1024 + 16 * lane;
+    const int r = o / (2 * D), sk = (o % (2 * D)) >> 4;
+    dma_k[k] = 2 * (r * D + 8 * (sk ^ k_swz<D>(r)));
+    const int d = o >> 7, sv = (o >> 4) & 7;
+    dma_v[k] = 2 * (d * ps + 8 * (sv ^ v_swz(d)));
+  }
 
   for (int qb = a.n_qblocks - 1 - (int)blockIdx.z; qb < nblk; qb += a.n_qblocks) {
     const int i0 = qb * QT;
@@ -119,11 +170,15 @@ void prefill_kernel(PrefillArgs a) {
         wave_hi = sp + i0 + i_hi;
       }
     }
-    float m_run[NT], l_run[NT];
+    // m_run: reference max (log2 units), neg_m: -m_run (0 while m_run = -inf),
+    // thr: raw-score threshold (m_run + 8) / c above which m_run must move.
+    float m_run[NT], l_run[NT], neg_m[NT], thr[NT];
     f32x4 acc[NT][D / 16];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       m_run[nt] = -INFINITY;
+      neg_m[nt] = 0.f;
+      thr[nt] = -INFINITY;
       l_run[nt] = 0.f;
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) acc[nt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -145,34 +200,50 @@ void prefill_kernel(PrefillArgs a) {
 
     // Copies the chunk at j0 into LDS buffer buf: this wave's share of the K
     // and V^T 1 KB blocks.  Keys past kv_hi (and unmapped pages) read page 0
-    // so every address stays inside the pool; the scores of such keys are
-    // masked and their V^T entries zeroed after the copy lands.
+    // or stay inside the chunk's page, so every address is inside the pool;
+    // the scores of such keys are masked and their V^T entries zeroed after
+    // the copy lands.
     auto issue = [&](int buf, int j0) {
       uint8_t* tK = lds + buf * tile_bytes<D>();
       uint8_t* tV = tK + k_tile_bytes<D>();
+      if (ps >= kChunk) {
+        // The chunk lies inside one page: one (scalar) page id and source base;
+        // the lane offsets within the page are fixed.
+        const int page = __builtin_amdgcn_readfirstlane(max(s_pg[(j0 >> log2ps) - pg0], 0));
+        const size_t base = (size_t)page * page_stride;
+        const int in_pg = j0 & (ps - 1);
+        const uint8_t* ks = reinterpret_cast<const uint8_t*>(kbase + base + (size_t)in_pg * D);
+        const uint8_t* vs = reinterpret_cast<const uint8_t*>(vbase + base + in_pg);
+#pragma unroll
+        for (int k = 0; k < dma_per_wave<D>(); ++k)
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const bf16_t*>(ks + dma_k[k]), (lds_void_ptr)(tK + (w * dma_per_wave<D>() + k) * 1024),
+                                           16, 0, 0);
+#pragma unroll
+        for (int k = 0; k < dma_per_wave<D>(); ++k)
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const bf16_t*>(vs + dma_v[k]), (lds_void_ptr)(tV + (w * dma_per_wave<D>() + k) * 1024),
+                                           16, 0, 0);
+        return;
+      }
+      // Small pages: a page id per lane and copy (branch-free, so the page id
+      // reads are issued together).
 #pragma unroll
       for (int k = 0; k < dma_per_wave<D>(); ++k) {
-        const int m = w * dma_per_wave<D>() + k;
-        const int o = m * 1024 + 16 * lane;
-        const int r = o / (2 * D), s = (o % (2 * D)) >> 4;
-        const int c = s ^ k_swz<D>(r);
+        const int r = (int)dma_k[k] / (2 * D), c8 = ((int)dma_k[k] % (2 * D)) >> 1;  // row, first dim
         const int j = j0 + r;
-        int page = j < kv_hi ? s_pg[(j >> log2ps) - pg0] : 0;
-        page = max(page, 0);
-        const bf16_t* src = kbase + (size_t)page * page_stride + (size_t)(j & (ps - 1)) * D + 8 * c;
-        __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(tK + m * 1024), 16, 0, 0);
+        const int pgv = s_pg[min((j >> log2ps) - pg0, n_pg - 1)];
+        const int page = j < kv_hi ? max(pgv, 0) : 0;
+        const bf16_t* src = kbase + (size_t)page * page_stride + (size_t)(j & (ps - 1)) * D + c8;
+        __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(tK + (w * dma_per_wave<D>() + k) * 1024), 16, 0, 0);
       }
 #pragma unroll
       for (int k = 0; k < dma_per_wave<D>(); ++k) {
-        const int m = w * dma_per_wave<D>() + k;
-        const int o = m * 1024 + 16 * lane;
-        const int d = o >> 7, s = (o >> 4) & 7;
-        const int g = s ^ v_swz(d);
+        const int o = (w * dma_per_wave<D>() + k) * 1024 + 16 * lane;
+        const int d = o >> 7, g = ((o >> 4) & 7) ^ v_swz(d);
         const int j = j0 + 8 * g;
-        int page = j < kv_hi ? s_pg[(j >> log2ps) - pg0] : 0;
-        page = max(page, 0);
+        const int pgv = s_pg[min((j >> log2ps) - pg0, n_pg - 1)];
+        const int page = j < kv_hi ? max(pgv, 0) : 0;
         const bf16_t* src = vbase + (size_t)page * page_stride + (size_t)d * ps + (j & (ps - 1));
-        __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(tV + m * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(tV + (w * dma_per_wave<D>() + k) * 1024), 16, 0, 0);
       }
     };
     // After a tail chunk lands: zero the V^T entries of keys >= kv_hi (stale
@@ -207,32 +278,24 @@ void prefill_kernel(PrefillArgs a) {
     for (int ck = 0; ck < n_chunks; ++ck) {
       const int j0 = j_start + ck * kChunk;
       if (ck + 1 < n_chunks) issue((ck + 1) & 1, j0 + kChunk);  // lands during this chunk's math
-      const uint8_t* tK = lds + (ck & 1) * tile_bytes<D>();
-      const uint8_t* tV = tK + k_tile_bytes<D>();
+      const int buf_off = (ck & 1) * tile_bytes<D>();
       const bool skip = wave_hi < 0 || j0 > wave_hi ||
                         (a.window > 0 && j0 + kChunk - 1 <= wave_lo - a.window);
       if (!skip) {
         const bool full = (j0 + kChunk - 1 <= wave_lo) && (a.window <= 0 || wave_hi - j0 < a.window);
-#pragma unroll 1
+#pragma unroll
         for (int h = 0; h < 2; ++h) {
           // ---- S^T = K Q^T for keys j0 + 32h + ..: MFMA rg row m holds key 8*(m/4) + 4*rg + m%4
           f32x4 S[NT][2];
 #pragma unroll
           for (int rg = 0; rg < 2; ++rg) {
-            const int r = 32 * h + 8 * (qc >> 2) + 4 * rg + (qc & 3);
-            const uint8_t* kr = tK + r * (2 * D);
-            const int sw = k_swz<D>(r);
-            {
-              const u32x4 kv = *reinterpret_cast<const u32x4*>(kr + 16 * (quad ^ sw));
+#pragma unroll
+            for (int c = 0; c < D / 32; ++c) {
+              const u32x4 kv = *reinterpret_cast<const u32x4*>(
+                  lds + ((buf_off + kofs[h][rg]) ^ (64 * c)));
 #pragma unroll
               for (int nt = 0; nt < NT; ++nt)
-                S[nt][rg] = mfma16x16x32(kv, qreg[nt][0], f32x4{0.f, 0.f, 0.f, 0.f});
-            }
-#pragma unroll
-            for (int c = 1; c < D / 32; ++c) {
-              const u32x4 kv = *reinterpret_cast<const u32x4*>(kr + 16 * ((4 * c + quad) ^ sw));
-#pragma unroll
-              for (int nt = 0; nt < NT; ++nt) S[nt][rg] = mfma16x16x32(kv, qreg[nt][c], S[nt][rg]);
+                S[nt][rg] = mfma16x16x32(kv, qreg[nt][c], c ? S[nt][rg] : f32x4{0.f, 0.f, 0.f, 0.f});
             }
           }
           // ---- element mask, only on chunks crossing the diagonal or the window edge
@@ -250,47 +313,47 @@ void prefill_kernel(PrefillArgs a) {
                 }
             }
           }
-          // ---- online softmax with a lazily moved reference max: p = 2^(s*c - m_ref)
-          // stays exact; m_ref only moves (and O is rescaled) when the running
-          // max exceeds it by more than 2^8, so p <= 256 and rescales are rare.
+          // ---- softmax against a lazily moved per-column reference max m_run:
+          // p = 2^(s*c - m_run).  m_run (with O and l rescaled) only moves when
+          // a score exceeds it by more than 2^8, which the common path detects
+          // with a per-lane compare against the column threshold (m_run + 8) / c
+          // -- no cross-lane work unless some lane of the wave crosses it.
+          bool need = false;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) need |= max8(S[nt]) > thr[nt];
+          if (__any(need)) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              const float mx = quad_max(max8(S[nt]));  // max over the column's 32 keys
+              const float m_new = fmaxf(m_run[nt], mx * a.scale_log2);
+              float alpha = 1.0f;
+              if (m_new > m_run[nt] + 8.0f) {
+                alpha = fast_exp2(m_run[nt] - m_new);  // 0 when m_run was -inf
+                m_run[nt] = m_new;
+                neg_m[nt] = -m_new;
+                thr[nt] = (m_new + 8.0f) * inv_c;
+              }
+              l_run[nt] *= alpha;
+#pragma unroll
+              for (int dt = 0; dt < D / 16; ++dt) acc[nt][dt] *= alpha;
+            }
+          }
           u32x4 pb[NT];
-          float alpha[NT];
-          bool resc = false;
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
-            float mx = fmaxf(fmaxf(fmaxf(S[nt][0][0], S[nt][0][1]), fmaxf(S[nt][0][2], S[nt][0][3])),
-                             fmaxf(fmaxf(S[nt][1][0], S[nt][1][1]), fmaxf(S[nt][1][2], S[nt][1][3])));
-            mx = fmaxf(mx, shfl_xor(mx, 16));
-            mx = fmaxf(mx, shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run[nt], mx * a.scale_log2);
-            const bool need = m_new > m_run[nt] + 8.0f;
-            alpha[nt] = need ? fast_exp2(m_run[nt] - m_new) : 1.0f;
-            if (need) m_run[nt] = m_new;
-            resc |= need;
-            const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
             float p[8];
-            float psum = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              p[e] = fast_exp2(fmaf(S[nt][e >> 2][e & 3], a.scale_log2, -m_use));
-              psum += p[e];
-            }
-            l_run[nt] = l_run[nt] * alpha[nt] + psum;
+            for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(S[nt][e >> 2][e & 3], a.scale_log2, neg_m[nt]));
             pb[nt] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-          }
-          if (__any(resc)) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-              for (int dt = 0; dt < D / 16; ++dt) acc[nt][dt] *= alpha[nt];
+            // fp32 row sum (summing the bf16 weights instead would cost the
+            // log-sum-exp up to 2^-9 of relative accuracy)
+            l_run[nt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
           }
           // ---- O^T += V^T P^T for this half; lane row d = 16*dt + qc, keys group 4h + quad
 #pragma unroll
           for (int dt = 0; dt < D / 16; ++dt) {
-            const int d = 16 * dt + qc;
-            const u32x4 vv =
-                *reinterpret_cast<const u32x4*>(tV + d * 128 + 16 * ((4 * h + quad) ^ v_swz(d)));
+            const u32x4 vv = *reinterpret_cast<const u32x4*>(lds + buf_off + vofs[h] + dt * 2048);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) acc[nt][dt] = mfma16x16x32(vv, pb[nt], acc[nt][dt]);
           }
