@@ -100,7 +100,7 @@ struct PrefillArgs {
   const bf16_t* vpool;
   float scale_log2;
   int window;
-  int q_tokens;   // query tokens per workgroup
+  int q_tokens;   // query tokens per work item
   int n_qblocks;  // grid extent over query blocks (grid-stride beyond it)
   bf16_t* out;
   float* lse;
@@ -126,5 +126,6 @@ DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_h
 
 // Query tokens per prefill workgroup for a GQA ratio.
 int prefill_q_tokens(int G, int head_dim);
+
 
 }  // namespace pkv

@@ -16,21 +16,22 @@
 // in flight while the current chunk is computed from the other LDS buffer,
 // with one wait + barrier per chunk.  Tiles are XOR-swizzled in 16-byte units
 // so that the MFMA operand reads of 16 rows hit 16 distinct bank groups.
-// Page ids of the workgroup's key range are staged in LDS once.
+// Page ids of the item's key range are staged in LDS once per item.
 //
-// Per 32-key half and column tile every wave computes
+// Per chunk and column tile every wave computes, for its two 32-key halves h,
 //
 //   S^T[32 keys][16 cols] = K[32][D] . Q^T[D][16]
 //   O^T[D][16 cols]      += V^T[D][32] . P^T[32][16]
 //
 // with the same operand layout as the decode kernel (a lane's 8 key scores
 // are directly its P^T k-slots).  The softmax keeps a reference max that only
-// moves when the running max outgrows it by 2^8, so the O accumulators are
-// rarely rescaled.  Chunks entirely above a wave's causal diagonal, or
-// entirely left of its sliding window, are skipped without MFMA work; chunks
-// entirely visible skip the per-element mask.  Query blocks are issued
-// longest-first, and the workgroups of one (sequence, kv head) share an XCD L2
-// when the kv head count is a multiple of 8 (grid x = kv head).
+// moves when some score outgrows it by 2^8, so the O accumulators are rarely
+// rescaled and the common path has no cross-lane work.  Chunks entirely above
+// a wave's causal diagonal, or entirely left of its sliding window, are
+// skipped without MFMA work; chunks entirely visible skip the element mask.
+//
+// Query blocks run longest-first on a (kv head, sequence, layer) grid; see
+// prefill_kernel and its launcher for the dispatch-order details.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -38,12 +39,16 @@ namespace pkv {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kChunk = 64;         // keys per pipeline step
-constexpr int kStagePages = 2048;  // page ids staged in LDS (>= pages_per_slot, host-checked)
+constexpr int kChunk = 64;                // keys per pipeline step
+constexpr int kStagePages = 2048;         // page ids staged in LDS (>= pages_per_slot, host-checked)
 
-// 16-column MFMA tiles per wave.
+// Waves per workgroup and 16-column MFMA tiles per wave: 4 waves of up to
+// 256 registers, two waves per SIMD (two workgroups per CU).  (8 waves of
+// one tile at 128 registers, four per SIMD, measured no faster and spills.)
+template <int D>
+constexpr int prefill_waves() { return 4; }
+template <int D>
+constexpr int prefill_threads() { return 64 * prefill_waves<D>(); }
 template <int D>
 constexpr int prefill_nt() { return D <= 128 ? 2 : 1; }
 
@@ -52,7 +57,7 @@ constexpr int k_tile_bytes() { return kChunk * D * 2; }   // [64 keys][D] bf16
 template <int D>
 constexpr int tile_bytes() { return 2 * k_tile_bytes<D>(); }  // + V^T [D][64 keys]
 template <int D>
-constexpr int dma_per_wave() { return D / 32; }  // 1 KB copies per wave, for K and for V each
+constexpr int dma_per_wave() { return D / (8 * prefill_waves<D>()); }  // 1 KB copies per wave, for K and V each
 
 // Swizzles (16-byte slot of a row).  K row r holds chunk c (dims 8c..8c+7) at
 // slot c ^ k_swz(r); V^T row d holds key group g (keys 8g..8g+7) at slot
@@ -88,329 +93,470 @@ __device__ __forceinline__ float quad_max(float v) {
   return vmax(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
 }
 
-template <int D, int NT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_kernel(PrefillArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int s_pg[kStagePages];
-  const int hk = blockIdx.x, n = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int qc = lane & 15, quad = lane >> 4;
-  const int G = a.G, QT = a.q_tokens;
-  const int ps = a.g.page_size, log2ps = a.g.log2ps, n_pages = a.g.n_pages;
-  const int a0 = a.cu_seqlens[n];
-  const int len = a.cu_seqlens[n + 1] - a0;
-  const int sp = a.start_pos ? a.start_pos[n] : 0;
-  const int slot = a.slots[n];
-  const bool idle = slot <= 0 || slot >= a.pt.max_slots || sp < 0;
-  const int nblk = (len + QT - 1) / QT;
-  const size_t blk = (size_t)ps * D;
-  const size_t page_stride = (size_t)a.g.n_kv * blk;
-  const bf16_t* kbase = a.kpool + hk * blk;
-  const bf16_t* vbase = a.vpool + hk * blk;
-  const int32_t* trow = a.pt.table + (size_t)(idle ? 0 : slot) * a.pt.pps;
-  const int cap = a.pt.pps * ps;
-  const float inv_c = 1.0f / a.scale_log2;  // scale > 0 (host-checked)
+// ---------------------------------------------------------------------------
+// Per-lane constants.
+template <int D>
+struct LaneConst {
   // LDS byte offsets (within a tile buffer) of this lane's MFMA operand rows.
   // K row r, dims chunk c sits at kofs ^ (64 * c): the row's swizzle is folded
   // into kofs and 64*c only flips bits inside the row.  V^T rows d = 16*dt + qc
   // share one swizzle across dt, so dt is a plain 2 KB step from vofs.
   int kofs[2][2], vofs[2];
+};
+
+// Source byte offsets of copy k of wave w for lane `lane`, relative to the
+// chunk's first key in its page.  The copy fills tile bytes m*1024 ..
+// m*1024+1023 (m = w*dpw + k), lane i the 16 bytes at +16*i.  K: tile row r
+// slot s holds dims 8*(s ^ k_swz(r)) ..  V^T: row d slot s holds keys
+// 8*(s ^ v_swz(d)) .. (V pages are d-major: element (d, key) at d*ps + key).
+// Recomputed at each use: a few ALU ops are cheaper than registers held
+// across the chunk math.
+template <int D>
+__device__ __forceinline__ uint32_t dma_k_off(int k, int lane, int w) {
+  const int o = (w * dma_per_wave<D>() + k) * 1024 + 16 * lane;
+  const int r = o / (2 * D), sk = (o % (2 * D)) >> 4;
+  return 2 * (r * D + 8 * (sk ^ k_swz<D>(r)));
+}
+template <int D>
+__device__ __forceinline__ uint32_t dma_v_off(int k, int lane, int w, int ps) {
+  const int o = (w * dma_per_wave<D>() + k) * 1024 + 16 * lane;
+  const int d = o >> 7, sv = (o >> 4) & 7;
+  return 2 * (d * ps + 8 * (sv ^ v_swz(d)));
+}
+
+template <int D>
+__device__ __forceinline__ void lane_const(LaneConst<D>& lc, int lane, int w, int ps) {
+  const int qc = lane & 15, quad = lane >> 4;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg) {
       const int r = 32 * h + 8 * (qc >> 2) + 4 * rg + (qc & 3);
-      kofs[h][rg] = r * (2 * D) + 16 * (quad ^ k_swz<D>(r));
+      lc.kofs[h][rg] = r * (2 * D) + 16 * (quad ^ k_swz<D>(r));
     }
-    vofs[h] = k_tile_bytes<D>() + qc * 128 + 16 * ((4 * h + quad) ^ v_swz(qc));
+    lc.vofs[h] = k_tile_bytes<D>() + qc * 128 + 16 * ((4 * h + quad) ^ v_swz(qc));
   }
-  // Source byte offsets of this lane's tile copies, relative to the chunk's
-  // first key in its page.  Copy k of the wave fills tile bytes m*1024 ..
-  // m*1024+1023 (m = w*dpw + k), lane i the 16 bytes at +16*i.  K: tile row r
-  // slot s holds dims 8*(s ^ k_swz(r)) ..  V^T: row d slot s holds keys
-  // 8*(s ^ v_swz(d)) .. (V pages are d-major: element (d, key) at d*ps + key).
-  uint32_t dma_k[dma_per_wave<D>()], dma_v[dma_per_wave<D>()];
+  (void)w;
+  (void)ps;
+}
+
+// ---------------------------------------------------------------------------
+// A work item: query block qb (tokens qb*QT ..) of sequence n against kv head
+// hk, and its key range [j_start, kv_hi) in 64-key chunks.
+struct Item {
+  int hk, n;
+  int a0, sp, i0, nq;
+  bool idle;  // padding sequence (slot 0 / out of range): output 0, lse -inf
+  int kv_hi, j_start, n_chunks, pg0, n_pg;
+  const int32_t* trow;
+};
+
+__device__ __forceinline__ void item_init(const PrefillArgs& a, int hk, int n, int qb, Item& it) {
+  it.hk = hk;
+  it.n = n;
+  it.a0 = a.cu_seqlens[n];
+  const int len = a.cu_seqlens[n + 1] - it.a0;
+  it.sp = a.start_pos ? a.start_pos[n] : 0;
+  const int slot = a.slots[n];
+  it.idle = slot <= 0 || slot >= a.pt.max_slots || it.sp < 0;
+  it.i0 = qb * a.q_tokens;
+  it.nq = min(a.q_tokens, len - it.i0);
+  it.trow = a.pt.table + (size_t)(it.idle ? 0 : slot) * a.pt.pps;
+  const int cap = a.pt.pps * a.g.page_size;
+  it.kv_hi = it.idle ? 0 : min(it.sp + it.i0 + it.nq, cap);
+  const int kv_lo = a.window > 0 ? max(0, it.sp + it.i0 - a.window + 1) : 0;
+  it.j_start = kv_lo & ~(kChunk - 1);
+  it.n_chunks = it.kv_hi > it.j_start ? (it.kv_hi - it.j_start + kChunk - 1) / kChunk : 0;
+  it.pg0 = it.j_start >> a.g.log2ps;
+  it.n_pg = it.n_chunks ? ((it.kv_hi - 1) >> a.g.log2ps) - it.pg0 + 1 : 0;
+}
+
+// An item parked in LDS (written by one thread) read back as uniform values.
+__device__ __forceinline__ Item load_item(const Item* p) {
+  const volatile int* v = reinterpret_cast<const volatile int*>(p);
+  constexpr int nw = sizeof(Item) / sizeof(int);
+  int x[nw];
+#pragma unroll
+  for (int i = 0; i < nw; ++i) x[i] = __builtin_amdgcn_readfirstlane(v[i]);
+  Item it;
+  __builtin_memcpy(&it, x, sizeof(Item));
+  return it;
+}
+
+// Page id as the copies use it: unmapped / out-of-range table entries become
+// -1 (read as page 0, whose keys are masked or zeroed).
+__device__ __forceinline__ int checked_page(int pg, int n_pages) {
+  return (pg >= 1 && pg < n_pages) ? pg : -1;
+}
+
+// Stage the item's page ids into s_pg (callers place the barriers).
+template <int D>
+__device__ __forceinline__ void stage_pages(const Item& it, int* s_pg, int tid, int n_pages) {
+  for (int i = tid; i < it.n_pg; i += prefill_threads<D>()) s_pg[i] = checked_page(it.trow[it.pg0 + i], n_pages);
+}
+
+// ---------------------------------------------------------------------------
+// This wave's query columns for an item: col = (w*NT + nt)*16 + qc maps to
+// token col/G, head col%G.
+template <int D, int NT>
+struct WaveQ {
+  u32x4 q[NT][D / 32];  // B operand of S^T = K Q^T (k-slot j of lane group g = dim 8g+j+32c)
+  int pcol[NT];         // query position of the lane's column (-1: no query)
+  int lo, hi;           // positions of the wave's first / last query (hi < 0: none)
+};
+
+template <int D, int NT>
+__device__ __forceinline__ void load_q(const PrefillArgs& a, const Item& it, int w, int lane,
+                                       WaveQ<D, NT>& wq) {
+  const int qc = lane & 15, quad = lane >> 4, G = a.G;
+  const int first_col = w * NT * 16;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int col = first_col + nt * 16 + qc;
+    const int i = col / G, g = col - i * G;
+    const bool valid = i < it.nq && !it.idle;
+    wq.pcol[nt] = valid ? it.sp + it.i0 + i : -1;
+    const bf16_t* qrow =
+        a.q + ((size_t)(it.a0 + it.i0 + (valid ? i : 0)) * a.n_q + it.hk * G + g) * D + 8 * quad;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const u32x4 v = load16(qrow + 32 * c);
+      wq.q[nt][c] = valid ? v : u32x4{0, 0, 0, 0};
+    }
+  }
+  wq.lo = 0x7fffffff;
+  wq.hi = -1;
+  const int i_lo = first_col / G;
+  const int i_hi = min(it.nq - 1, (first_col + NT * 16 - 1) / G);
+  if (!it.idle && i_lo < it.nq) {
+    wq.lo = it.sp + it.i0 + i_lo;
+    wq.hi = it.sp + it.i0 + i_hi;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Copies the chunk at j0 into LDS buffer buf: this wave's share of the K and
+// V^T 1 KB blocks.  Keys past kv_hi (and unmapped pages) read page 0 or stay
+// inside the chunk's page, so every address is inside the pool; the scores of
+// such keys are masked and their V^T entries zeroed after the copy lands.
+template <int D>
+__device__ __forceinline__ void issue_tile(const PrefillArgs& a, const Item& it, const int* s_pg,
+                                           uint8_t* lds, int buf, int j0, const LaneConst<D>& lc,
+                                           int lane, int w) {
+  const int ps = a.g.page_size, log2ps = a.g.log2ps;
+  const size_t blk = (size_t)ps * D;
+  const size_t page_stride = (size_t)a.g.n_kv * blk;
+  const bf16_t* kbase = a.kpool + it.hk * blk;
+  const bf16_t* vbase = a.vpool + it.hk * blk;
+  uint8_t* tK = lds + buf * tile_bytes<D>();
+  uint8_t* tV = tK + k_tile_bytes<D>();
+  if (ps >= kChunk) {
+    // The chunk lies inside one page: one (scalar) page id and source base;
+    // the lane offsets within the page are fixed.
+    const int page = __builtin_amdgcn_readfirstlane(max(s_pg[(j0 >> log2ps) - it.pg0], 0));
+    const size_t base = (size_t)page * page_stride;
+    const int in_pg = j0 & (ps - 1);
+    const uint8_t* ks = reinterpret_cast<const uint8_t*>(kbase + base + (size_t)in_pg * D);
+    const uint8_t* vs = reinterpret_cast<const uint8_t*>(vbase + base + in_pg);
+#pragma unroll
+    for (int k = 0; k < dma_per_wave<D>(); ++k)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const bf16_t*>(ks + dma_k_off<D>(k, lane, w)),
+                                       (lds_void_ptr)(tK + (w * dma_per_wave<D>() + k) * 1024),
+                                       16, 0, 0);
+#pragma unroll
+    for (int k = 0; k < dma_per_wave<D>(); ++k)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const bf16_t*>(vs + dma_v_off<D>(k, lane, w, ps)),
+                                       (lds_void_ptr)(tV + (w * dma_per_wave<D>() + k) * 1024),
+                                       16, 0, 0);
+    return;
+  }
+  // Small pages: a page id per lane and copy (branch-free, so the page id
+  // reads are issued together).
+#pragma unroll
+  for (int k = 0; k < dma_per_wave<D>(); ++k) {
+    const int off = (int)dma_k_off<D>(k, lane, w);
+    const int r = off / (2 * D), c8 = (off % (2 * D)) >> 1;  // row, first dim
+    const int j = j0 + r;
+    const int pgv = s_pg[min((j >> log2ps) - it.pg0, it.n_pg - 1)];
+    const int page = j < it.kv_hi ? max(pgv, 0) : 0;
+    const bf16_t* src = kbase + (size_t)page * page_stride + (size_t)(j & (ps - 1)) * D + c8;
+    __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(tK + (w * dma_per_wave<D>() + k) * 1024), 16, 0, 0);
+  }
 #pragma unroll
   for (int k = 0; k < dma_per_wave<D>(); ++k) {
     const int o = (w * dma_per_wave<D>() + k) * 1024 + 16 * lane;
-    const int r = o / (2 * D), sk = (o % (2 * D)) >> 4;
-    dma_k[k] = 2 * (r * D + 8 * (sk ^ k_swz<D>(r)));
-    const int d = o >> 7, sv = (o >> 4) & 7;
-    dma_v[k] = 2 * (d * ps + 8 * (sv ^ v_swz(d)));
+    const int d = o >> 7, g = ((o >> 4) & 7) ^ v_swz(d);
+    const int j = j0 + 8 * g;
+    const int pgv = s_pg[min((j >> log2ps) - it.pg0, it.n_pg - 1)];
+    const int page = j < it.kv_hi ? max(pgv, 0) : 0;
+    const bf16_t* src = vbase + (size_t)page * page_stride + (size_t)d * ps + (j & (ps - 1));
+    __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(tV + (w * dma_per_wave<D>() + k) * 1024), 16, 0, 0);
   }
+}
 
-  for (int qb = a.n_qblocks - 1 - (int)blockIdx.z; qb < nblk; qb += a.n_qblocks) {
-    const int i0 = qb * QT;
-    const int nq = min(QT, len - i0);
-    // ---- columns of this wave: col = (w*NT + nt)*16 + qc -> token col/G, head col%G
-    int pcol[NT];
-    u32x4 qreg[NT][D / 32];
-    const int first_col = w * NT * 16;
+// After a tail chunk lands: zero the V^T entries of keys >= kv_hi (stale page
+// rows may hold anything, and 0 * NaN would poison P.V).  Returns whether it
+// wrote (callers then place a barrier).
+template <int D>
+__device__ __forceinline__ bool zero_tail(uint8_t* lds, int buf, int j0, int kv_hi, int tid) {
+  const int nvk = kv_hi - j0;
+  if (nvk >= kChunk) return false;
+  uint8_t* tV = lds + buf * tile_bytes<D>() + k_tile_bytes<D>();
+  for (int idx = tid; idx < D * 8; idx += prefill_threads<D>()) {
+    const int d = idx >> 3, s = idx & 7;
+    const int g = s ^ v_swz(d);
+    const int nv = nvk - 8 * g;
+    if (nv >= 8) continue;
+    u32x4* p = reinterpret_cast<u32x4*>(tV + d * 128 + 16 * s);
+    u32x4 v = *p;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int col = first_col + nt * 16 + qc;
-      const int i = col / G, g = col - i * G;
-      const bool valid = i < nq && !idle;
-      pcol[nt] = valid ? sp + i0 + i : -1;
-      const bf16_t* qrow = a.q + ((size_t)(a0 + i0 + (valid ? i : 0)) * a.n_q + hk * G + g) * D +
-                           8 * quad;
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t m = (2 * e < nv ? 0x0000ffffu : 0u) | (2 * e + 1 < nv ? 0xffff0000u : 0u);
+      v[e] &= m;
+    }
+    *p = v;
+  }
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Online-softmax state of a wave's NT column tiles.
+template <int D, int NT>
+struct SoftmaxAcc {
+  f32x4 o[NT][D / 16];  // O^T accumulators: lane rows d = 16*dt + 4*(lane/16) + r, column lane%16
+  float m_run[NT];      // reference max (log2 units)
+  float neg_m[NT];      // -m_run (0 while m_run = -inf)
+  float thr[NT];        // raw-score threshold (m_run + 8) / c above which m_run must move
+  float l_run[NT];      // this lane's share of the row sum
+};
+
+template <int D, int NT>
+__device__ __forceinline__ void acc_init(SoftmaxAcc<D, NT>& s) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    s.m_run[nt] = -INFINITY;
+    s.neg_m[nt] = 0.f;
+    s.thr[nt] = -INFINITY;
+    s.l_run[nt] = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) s.o[nt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// One 64-key chunk (keys j0 ..) from LDS buffer offset buf_off for this wave.
+template <int D, int NT>
+__device__ __forceinline__ void chunk_math(const PrefillArgs& a, const uint8_t* lds, int buf_off,
+                                           int j0, const LaneConst<D>& lc, const WaveQ<D, NT>& wq,
+                                           int quad, float inv_c, SoftmaxAcc<D, NT>& sa) {
+  const bool skip = wq.hi < 0 || j0 > wq.hi || (a.window > 0 && j0 + kChunk - 1 <= wq.lo - a.window);
+  if (skip) return;
+  const bool full = (j0 + kChunk - 1 <= wq.lo) && (a.window <= 0 || wq.hi - j0 < a.window);
+  // ---- S^T = K Q^T for the chunk's two 32-key halves h: MFMA rg row m holds
+  // key j0 + 32h + 8*(m/4) + 4*rg + m%4
+  f32x4 S[2][NT][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) {
-        const u32x4 v = load16(qrow + 32 * c);
-        qreg[nt][c] = valid ? v : u32x4{0, 0, 0, 0};
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(lds + ((buf_off + lc.kofs[h][rg]) ^ (64 * c)));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          S[h][nt][rg] = mfma16x16x32(kv, wq.q[nt][c], c ? S[h][nt][rg] : f32x4{0.f, 0.f, 0.f, 0.f});
       }
     }
-    int wave_lo = 0x7fffffff, wave_hi = -1;
-    {
-      const int i_lo = first_col / G;
-      const int i_hi = min(nq - 1, (first_col + NT * 16 - 1) / G);
-      if (!idle && i_lo < nq) {
-        wave_lo = sp + i0 + i_lo;
-        wave_hi = sp + i0 + i_hi;
-      }
-    }
-    // m_run: reference max (log2 units), neg_m: -m_run (0 while m_run = -inf),
-    // thr: raw-score threshold (m_run + 8) / c above which m_run must move.
-    float m_run[NT], l_run[NT], neg_m[NT], thr[NT];
-    f32x4 acc[NT][D / 16];
+  // ---- element mask, only on chunks crossing the diagonal or the window edge
+  if (!full) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      m_run[nt] = -INFINITY;
-      neg_m[nt] = 0.f;
-      thr[nt] = -INFINITY;
-      l_run[nt] = 0.f;
+      const int pc = wq.pcol[nt];
+      const int jmin = a.window > 0 ? pc - a.window + 1 : -0x7fffffff;
 #pragma unroll
-      for (int i = 0; i < D / 16; ++i) acc[nt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    // ---- key range of the workgroup
-    const int kv_hi = idle ? 0 : min(sp + i0 + nq, cap);
-    const int kv_lo = (a.window > 0) ? max(0, sp + i0 - a.window + 1) : 0;
-    const int j_start = kv_lo & ~(kChunk - 1);
-    const int n_chunks = kv_hi > j_start ? (kv_hi - j_start + kChunk - 1) / kChunk : 0;
-    const int pg0 = j_start >> log2ps;
-    const int n_pg = n_chunks ? ((kv_hi - 1) >> log2ps) - pg0 + 1 : 0;
-
-    __syncthreads();  // previous block's tiles and page ids are consumed
-    for (int i = tid; i < n_pg; i += kThreads) {
-      const int pg = trow[pg0 + i];
-      s_pg[i] = (pg >= 1 && pg < n_pages) ? pg : -1;
-    }
-    __syncthreads();
-
-    // Copies the chunk at j0 into LDS buffer buf: this wave's share of the K
-    // and V^T 1 KB blocks.  Keys past kv_hi (and unmapped pages) read page 0
-    // or stay inside the chunk's page, so every address is inside the pool;
-    // the scores of such keys are masked and their V^T entries zeroed after
-    // the copy lands.
-    auto issue = [&](int buf, int j0) {
-      uint8_t* tK = lds + buf * tile_bytes<D>();
-      uint8_t* tV = tK + k_tile_bytes<D>();
-      if (ps >= kChunk) {
-        // The chunk lies inside one page: one (scalar) page id and source base;
-        // the lane offsets within the page are fixed.
-        const int page = __builtin_amdgcn_readfirstlane(max(s_pg[(j0 >> log2ps) - pg0], 0));
-        const size_t base = (size_t)page * page_stride;
-        const int in_pg = j0 & (ps - 1);
-        const uint8_t* ks = reinterpret_cast<const uint8_t*>(kbase + base + (size_t)in_pg * D);
-        const uint8_t* vs = reinterpret_cast<const uint8_t*>(vbase + base + in_pg);
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int k = 0; k < dma_per_wave<D>(); ++k)
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const bf16_t*>(ks + dma_k[k]), (lds_void_ptr)(tK + (w * dma_per_wave<D>() + k) * 1024),
-                                           16, 0, 0);
+        for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
-        for (int k = 0; k < dma_per_wave<D>(); ++k)
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const bf16_t*>(vs + dma_v[k]), (lds_void_ptr)(tV + (w * dma_per_wave<D>() + k) * 1024),
-                                           16, 0, 0);
-        return;
-      }
-      // Small pages: a page id per lane and copy (branch-free, so the page id
-      // reads are issued together).
-#pragma unroll
-      for (int k = 0; k < dma_per_wave<D>(); ++k) {
-        const int r = (int)dma_k[k] / (2 * D), c8 = ((int)dma_k[k] % (2 * D)) >> 1;  // row, first dim
-        const int j = j0 + r;
-        const int pgv = s_pg[min((j >> log2ps) - pg0, n_pg - 1)];
-        const int page = j < kv_hi ? max(pgv, 0) : 0;
-        const bf16_t* src = kbase + (size_t)page * page_stride + (size_t)(j & (ps - 1)) * D + c8;
-        __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(tK + (w * dma_per_wave<D>() + k) * 1024), 16, 0, 0);
-      }
-#pragma unroll
-      for (int k = 0; k < dma_per_wave<D>(); ++k) {
-        const int o = (w * dma_per_wave<D>() + k) * 1024 + 16 * lane;
-        const int d = o >> 7, g = ((o >> 4) & 7) ^ v_swz(d);
-        const int j = j0 + 8 * g;
-        const int pgv = s_pg[min((j >> log2ps) - pg0, n_pg - 1)];
-        const int page = j < kv_hi ? max(pgv, 0) : 0;
-        const bf16_t* src = vbase + (size_t)page * page_stride + (size_t)d * ps + (j & (ps - 1));
-        __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(tV + (w * dma_per_wave<D>() + k) * 1024), 16, 0, 0);
-      }
-    };
-    // After a tail chunk lands: zero the V^T entries of keys >= kv_hi (stale
-    // page rows may hold anything, and 0 * NaN would poison P.V).
-    auto zero_tail = [&](int buf, int j0) {
-      const int nvk = kv_hi - j0;
-      if (nvk >= kChunk) return;
-      uint8_t* tV = lds + buf * tile_bytes<D>() + k_tile_bytes<D>();
-      for (int idx = tid; idx < D * 8; idx += kThreads) {
-        const int d = idx >> 3, s = idx & 7;
-        const int g = s ^ v_swz(d);
-        const int nv = nvk - 8 * g;
-        if (nv >= 8) continue;
-        u32x4* p = reinterpret_cast<u32x4*>(tV + d * 128 + 16 * s);
-        u32x4 v = *p;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t m = (2 * e < nv ? 0x0000ffffu : 0u) | (2 * e + 1 < nv ? 0xffff0000u : 0u);
-          v[e] &= m;
-        }
-        *p = v;
-      }
-    };
-
-    if (n_chunks > 0) issue(0, j_start);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
-    __syncthreads();
-    if (n_chunks > 0 && j_start + kChunk > kv_hi) {
-      zero_tail(0, j_start);
-      __syncthreads();
-    }
-    for (int ck = 0; ck < n_chunks; ++ck) {
-      const int j0 = j_start + ck * kChunk;
-      if (ck + 1 < n_chunks) issue((ck + 1) & 1, j0 + kChunk);  // lands during this chunk's math
-      const int buf_off = (ck & 1) * tile_bytes<D>();
-      const bool skip = wave_hi < 0 || j0 > wave_hi ||
-                        (a.window > 0 && j0 + kChunk - 1 <= wave_lo - a.window);
-      if (!skip) {
-        const bool full = (j0 + kChunk - 1 <= wave_lo) && (a.window <= 0 || wave_hi - j0 < a.window);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          // ---- S^T = K Q^T for keys j0 + 32h + ..: MFMA rg row m holds key 8*(m/4) + 4*rg + m%4
-          f32x4 S[NT][2];
-#pragma unroll
-          for (int rg = 0; rg < 2; ++rg) {
-#pragma unroll
-            for (int c = 0; c < D / 32; ++c) {
-              const u32x4 kv = *reinterpret_cast<const u32x4*>(
-                  lds + ((buf_off + kofs[h][rg]) ^ (64 * c)));
-#pragma unroll
-              for (int nt = 0; nt < NT; ++nt)
-                S[nt][rg] = mfma16x16x32(kv, qreg[nt][c], c ? S[nt][rg] : f32x4{0.f, 0.f, 0.f, 0.f});
-            }
+          for (int e = 0; e < 4; ++e) {
+            const int j = j0 + 32 * h + 8 * quad + 4 * rg + e;
+            if (j > pc || j < jmin) S[h][nt][rg][e] = -INFINITY;
           }
-          // ---- element mask, only on chunks crossing the diagonal or the window edge
-          if (!full) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-              const int pc = pcol[nt];
-              const int jmin = a.window > 0 ? pc - a.window + 1 : -0x7fffffff;
-#pragma unroll
-              for (int rg = 0; rg < 2; ++rg)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const int j = j0 + 32 * h + 8 * quad + 4 * rg + e;
-                  if (j > pc || j < jmin) S[nt][rg][e] = -INFINITY;
-                }
-            }
-          }
-          // ---- softmax against a lazily moved per-column reference max m_run:
-          // p = 2^(s*c - m_run).  m_run (with O and l rescaled) only moves when
-          // a score exceeds it by more than 2^8, which the common path detects
-          // with a per-lane compare against the column threshold (m_run + 8) / c
-          // -- no cross-lane work unless some lane of the wave crosses it.
-          bool need = false;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) need |= max8(S[nt]) > thr[nt];
-          if (__any(need)) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-              const float mx = quad_max(max8(S[nt]));  // max over the column's 32 keys
-              const float m_new = fmaxf(m_run[nt], mx * a.scale_log2);
-              float alpha = 1.0f;
-              if (m_new > m_run[nt] + 8.0f) {
-                alpha = fast_exp2(m_run[nt] - m_new);  // 0 when m_run was -inf
-                m_run[nt] = m_new;
-                neg_m[nt] = -m_new;
-                thr[nt] = (m_new + 8.0f) * inv_c;
-              }
-              l_run[nt] *= alpha;
-#pragma unroll
-              for (int dt = 0; dt < D / 16; ++dt) acc[nt][dt] *= alpha;
-            }
-          }
-          u32x4 pb[NT];
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(S[nt][e >> 2][e & 3], a.scale_log2, neg_m[nt]));
-            pb[nt] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-            // fp32 row sum (summing the bf16 weights instead would cost the
-            // log-sum-exp up to 2^-9 of relative accuracy)
-            l_run[nt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-          }
-          // ---- O^T += V^T P^T for this half; lane row d = 16*dt + qc, keys group 4h + quad
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) {
-            const u32x4 vv = *reinterpret_cast<const u32x4*>(lds + buf_off + vofs[h] + dt * 2048);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) acc[nt][dt] = mfma16x16x32(vv, pb[nt], acc[nt][dt]);
-          }
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk's copies have landed
-      __syncthreads();
-      if (ck + 1 < n_chunks && j0 + 2 * kChunk > kv_hi) {
-        zero_tail((ck + 1) & 1, j0 + kChunk);
-        __syncthreads();
-      }
-    }
-
-    // ---- normalise and store
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float l = l_run[nt];
-      l += shfl_xor(l, 16);
-      l += shfl_xor(l, 32);
-      const int col = first_col + nt * 16 + qc;
-      const int i = col / G, g = col - i * G;
-      if (i >= nq) continue;
-      const float inv = l > 0.f ? 1.0f / l : 0.f;
-      bf16_t* orow = a.out + ((size_t)(a0 + i0 + i) * a.n_q + hk * G + g) * D;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const f32x4 o = acc[nt][dt];
-        uint2 pk2;
-        pk2.x = pack_bf16x2(o[0] * inv, o[1] * inv);
-        pk2.y = pack_bf16x2(o[2] * inv, o[3] * inv);
-        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * quad) = pk2;
-      }
-      if (a.lse && quad == 0)
-        a.lse[(size_t)(a0 + i0 + i) * a.n_q + hk * G + g] =
-            l > 0.f ? (m_run[nt] + __log2f(l)) * kLn2 : -INFINITY;
     }
   }
+  // ---- softmax against a lazily moved per-column reference max m_run:
+  // p = 2^(s*c - m_run).  m_run (with O and l rescaled) only moves when a
+  // score exceeds it by more than 2^8, which the common path detects with a
+  // per-lane compare against the column threshold (m_run + 8) / c -- no
+  // cross-lane work unless some lane of the wave crosses it.
+  float lmax[NT];
+  bool need = false;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    lmax[nt] = vmax(max8(S[0][nt]), max8(S[1][nt]));
+    need |= lmax[nt] > sa.thr[nt];
+  }
+  if (__any(need)) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float mx = quad_max(lmax[nt]);  // max over the column's 64 keys
+      const float m_new = fmaxf(sa.m_run[nt], mx * a.scale_log2);
+      float alpha = 1.0f;
+      if (m_new > sa.m_run[nt] + 8.0f) {
+        alpha = fast_exp2(sa.m_run[nt] - m_new);  // 0 when m_run was -inf
+        sa.m_run[nt] = m_new;
+        sa.neg_m[nt] = -m_new;
+        sa.thr[nt] = (m_new + 8.0f) * inv_c;
+      }
+      sa.l_run[nt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) sa.o[nt][dt] *= alpha;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    u32x4 pb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(S[h][nt][e >> 2][e & 3], a.scale_log2, sa.neg_m[nt]));
+      pb[nt] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                     pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+      // fp32 row sum (summing the bf16 weights instead would cost the
+      // log-sum-exp up to 2^-9 of relative accuracy)
+      sa.l_run[nt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    }
+    // ---- O^T += V^T P^T for this half; lane row d = 16*dt + qc, keys group 4h + quad
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const u32x4 vv = *reinterpret_cast<const u32x4*>(lds + buf_off + lc.vofs[h] + dt * 2048);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sa.o[nt][dt] = mfma16x16x32(vv, pb[nt], sa.o[nt][dt]);
+    }
+  }
+}
+
+// Normalise and store the wave's columns of an item (padding rows: 0 / -inf).
+template <int D, int NT>
+__device__ __forceinline__ void store_out(const PrefillArgs& a, const Item& it, int w, int lane,
+                                          const SoftmaxAcc<D, NT>& sa) {
+  const int qc = lane & 15, quad = lane >> 4, G = a.G;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float l = sa.l_run[nt];
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    const int col = w * NT * 16 + nt * 16 + qc;
+    const int i = col / G, g = col - i * G;
+    if (i >= it.nq) continue;
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    bf16_t* orow = a.out + ((size_t)(it.a0 + it.i0 + i) * a.n_q + it.hk * G + g) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const f32x4 o = sa.o[nt][dt];
+      uint2 pk2;
+      pk2.x = pack_bf16x2(o[0] * inv, o[1] * inv);
+      pk2.y = pack_bf16x2(o[2] * inv, o[3] * inv);
+      *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * quad) = pk2;
+    }
+    if (a.lse && quad == 0)
+      a.lse[(size_t)(it.a0 + it.i0 + i) * a.n_q + it.hk * G + g] =
+          l > 0.f ? (sa.m_run[nt] + __log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One work item end to end: stage its page ids, stream its key chunks through
+// the two LDS tile buffers (the next chunk's copy in flight while the current
+// one is computed), normalise and store.
+template <int D, int NT>
+__device__ __forceinline__ void run_item(const PrefillArgs& a, int hk, int n, int qb, uint8_t* lds,
+                                         int* s_pg, const LaneConst<D>& lc, int tid, int lane,
+                                         int w, float inv_c) {
+  const int quad = lane >> 4;
+  Item it;
+  item_init(a, hk, n, qb, it);
+  WaveQ<D, NT> wq;
+  load_q<D, NT>(a, it, w, lane, wq);
+  SoftmaxAcc<D, NT> sa;
+  acc_init(sa);
+  __syncthreads();  // the previous item's tiles and page ids are consumed
+  stage_pages<D>(it, s_pg, tid, a.g.n_pages);
+  __syncthreads();
+  if (it.n_chunks > 0) issue_tile<D>(a, it, s_pg, lds, 0, it.j_start, lc, lane, w);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+  __syncthreads();
+  if (it.n_chunks > 0 && zero_tail<D>(lds, 0, it.j_start, it.kv_hi, tid)) __syncthreads();
+  for (int ck = 0; ck < it.n_chunks; ++ck) {
+    const int j0 = it.j_start + ck * kChunk;
+    if (ck + 1 < it.n_chunks) issue_tile<D>(a, it, s_pg, lds, (ck + 1) & 1, j0 + kChunk, lc, lane, w);
+    chunk_math<D, NT>(a, lds, (ck & 1) * tile_bytes<D>(), j0, lc, wq, quad, inv_c, sa);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk's copies have landed
+    __syncthreads();
+    if (ck + 1 < it.n_chunks && zero_tail<D>(lds, (ck + 1) & 1, j0 + kChunk, it.kv_hi, tid))
+      __syncthreads();
+  }
+  store_out<D, NT>(a, it, w, lane, sa);
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup per (kv head, sequence, layer of query blocks); layers run
+// from the last query block down, so the longest items start first (a
+// workgroup whose layer exceeds its sequence's block count exits at once).
+// Grid x = kv head: with n_kv a multiple of 8 the XCDs (every 8th workgroup)
+// each keep their heads' K/V in their own L2.
+template <int D, int NT>
+__global__ __launch_bounds__(prefill_threads<D>())
+__attribute__((amdgpu_waves_per_eu(prefill_waves<D>() / 2, prefill_waves<D>() / 2)))
+void prefill_kernel(PrefillArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int s_pg[kStagePages];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float inv_c = 1.0f / a.scale_log2;  // scale > 0 (host-checked)
+  LaneConst<D> lc;
+  lane_const<D>(lc, lane, w, a.g.page_size);
+  const int hk = blockIdx.x, n = blockIdx.y;
+  if (n >= a.n_seqs) return;  // padding row of the grid (odd y extent)
+  const int len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
+  const int nblk = (len + a.q_tokens - 1) / a.q_tokens;
+  for (int qb = a.n_qblocks - 1 - (int)blockIdx.z; qb < nblk; qb += a.n_qblocks)
+    run_item<D, NT>(a, hk, n, qb, lds, s_pg, lc, tid, lane, w, inv_c);
+}
+
+// ---------------------------------------------------------------------------
+template <typename K>
+hipError_t set_lds_limit(K* kernel, int bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
 template <int D>
 hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t st) {
   constexpr int NT = prefill_nt<D>();
-  const size_t lds = 2 * (size_t)tile_bytes<D>();
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&prefill_kernel<D, NT>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const int lds = 2 * tile_bytes<D>();
+  static const hipError_t attr = set_lds_limit(&prefill_kernel<D, NT>, lds);
   if (attr != hipSuccess) return attr;
-  dim3 grid(a.g.n_kv, a.n_seqs, a.n_qblocks);
-  hipLaunchKernelGGL((prefill_kernel<D, NT>), grid, dim3(kThreads), lds, st, a);
+  // An XCD hands its workgroups to its 4 shader engines round-robin and
+  // dispatches in order, stalling when the next workgroup's engine is full.
+  // With an even y extent every layer would send the same sequences to the
+  // same engine (engine = sequence mod 4 when the kv heads fill the XCDs), so
+  // long prompts pile onto one engine; an odd extent rotates each sequence
+  // across the engines layer by layer (measured 10% faster on ragged
+  // batches).  (A 1-D grid in exact cost order, mapped in-kernel, balanced
+  // the engines too but its per-workgroup set-up cost more than it saved.)
+  dim3 grid(a.g.n_kv, a.n_seqs | 1, a.n_qblocks);
+  hipLaunchKernelGGL((prefill_kernel<D, NT>), grid, dim3(prefill_threads<D>()), lds, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int prefill_q_tokens(int G, int head_dim) {
-  const int nt = head_dim <= 128 ? 2 : 1;
-  return (kWaves * nt * 16) / G;
+  switch (head_dim) {
+    case 64: return prefill_waves<64>() * prefill_nt<64>() * 16 / G;
+    case 128: return prefill_waves<128>() * prefill_nt<128>() * 16 / G;
+    default: return prefill_waves<256>() * prefill_nt<256>() * 16 / G;
+  }
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {

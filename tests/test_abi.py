@@ -94,6 +94,11 @@ def test_append_and_prefill_argument_checks():
     bad = _lib.Prologue(None, 1, 1e-6, 1, 1, 16, 1, 1)
     assert L.pkv_attn_prefill(1, 4, 1, 1, None, 1, 8, 8, _pt(), ctypes.byref(cd), 1, 1, 0.1, 0,
                               ctypes.byref(bad), 1, None, None, 0, None) == 1
+    # prefill scale must be > 0
+    assert L.pkv_attn_prefill(1, 4, 1, 1, None, 1, 8, 8, _pt(), ctypes.byref(cd), 1, 1,
+                              -0.1, 0, None, 1, None, None, 0, None) == 1
+    assert L.pkv_attn_prefill(1, 4, 1, 1, None, 1, 8, 8, _pt(), ctypes.byref(cd), 1, 1,
+                              0.0, 0, None, 1, None, None, 0, None) == 1
     assert L.pkv_rope_table(None, 1, 8, 64, 1e6, None) == 1
     assert L.pkv_rope_table(1, 1, 8, 63, 1e6, None) == 1
 

@@ -47,20 +47,19 @@ def _case(name, seed=0):
                              slots=slots, max_slots=4 if slots else None, window=window)
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_prefill_no_prologue_matches_oracle(name):
-    case = _case(name)
-    kp, vp, table, okp, ovp = _pools_with_prefix(case)
-    tsl, tpos = case.token_slots(), case.token_pos()
-    pkv.append(dev_bits(case.k), dev_bits(case.v), dev_i32(tsl), dev_i32(tpos), table, kp, vp)
-    oracle.append(okp, ovp, case.table, case.k, case.v, tsl, tpos)
+def _run_no_prologue(case, kp, vp, table, hint=None):
     q = dev_bits(case.q)
     lse = torch.empty((case.T, case.n_q), dtype=torch.float32, device=q.device)
     out = pkv.attn_prefill(q, dev_i32(case.cu_seqlens), dev_i32(case.slots), table, kp, vp,
                            scale=case.scale, window=case.window,
                            start_pos=dev_i32(case.start_pos),
-                           max_seqlen_q_hint=int(np.diff(case.cu_seqlens).max()), lse=lse)
+                           max_seqlen_q_hint=hint or int(np.diff(case.cu_seqlens).max()),
+                           lse=lse)
     torch.cuda.synchronize()
+    return q, out, lse
+
+
+def _check_no_prologue(case, q, out, lse, okp, ovp, name):
     ref, ref_lse = oracle.attn_prefill(case.q, okp, ovp, case.table, case.cu_seqlens,
                                        case.slots, case.start_pos, case.scale, case.window)
     assert_attn_close(host_f64(out), ref, name)
@@ -70,8 +69,55 @@ def test_prefill_no_prologue_matches_oracle(name):
     assert np.max(np.abs(g_lse[fin] - ref_lse[fin]), initial=0.0) <= 1e-3
     # q untouched without a prologue; padding rows exactly zero
     assert np.array_equal(host_bits(q), case.q)
-    pad = tsl == 0
+    pad = case.token_slots() == 0
     assert np.all(host_bits(out)[pad] == 0)
+
+
+def _append_tokens(case, kp, vp, table, okp, ovp):
+    tsl, tpos = case.token_slots(), case.token_pos()
+    pkv.append(dev_bits(case.k), dev_bits(case.v), dev_i32(tsl), dev_i32(tpos), table, kp, vp)
+    oracle.append(okp, ovp, case.table, case.k, case.v, tsl, tpos)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_prefill_no_prologue_matches_oracle(name):
+    case = _case(name)
+    kp, vp, table, okp, ovp = _pools_with_prefix(case)
+    _append_tokens(case, kp, vp, table, okp, ovp)
+    q, out, lse = _run_no_prologue(case, kp, vp, table)
+    _check_no_prologue(case, q, out, lse, okp, ovp, name)
+
+
+def test_prefill_many_sequences_hint_below_longest():
+    """531 prompts, a max_seqlen_q_hint below the longest (grid-stride path)."""
+    rng = np.random.default_rng(21)
+    lengths = [int(x) for x in rng.integers(1, 12, size=530)] + [70]
+    case = make_prefill_case(8, 2, 64, 16, lengths, seed=2100, max_slots=len(lengths) + 1)
+    kp, vp, table, okp, ovp = _pools_with_prefix(case)
+    _append_tokens(case, kp, vp, table, okp, ovp)
+    q, out, lse = _run_no_prologue(case, kp, vp, table, hint=8)
+    _check_no_prologue(case, q, out, lse, okp, ovp, "530 prompts")
+
+
+def test_prefill_long_prompt_sampled():
+    """A 4200-token prompt beside a short one (525 query blocks), sampled rows."""
+    # n_q 16 over 1 kv head: 8 query tokens per item, so 4200 tokens = 525 blocks
+    lengths = [4200, 33]
+    case = make_prefill_case(16, 1, 64, 64, lengths, seed=2200)
+    kp, vp, table, okp, ovp = _pools_with_prefix(case)
+    _append_tokens(case, kp, vp, table, okp, ovp)
+    q, out, lse = _run_no_prologue(case, kp, vp, table)
+    g = host_f64(out)
+    gl = lse.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(5)
+    rows = np.concatenate([[0, 4199, 4200, 4232], rng.choice(case.T, size=8, replace=False)])
+    for t in rows:
+        n = int(np.searchsorted(case.cu_seqlens, t, side="right") - 1)
+        p = t - int(case.cu_seqlens[n])
+        K, V = oracle.gather_kv(okp, ovp, case.table, int(case.slots[n]), p + 1)
+        ref, ref_lse = oracle.attend_rows(oracle.bf16_bits_to_f64(case.q[t]), K, V, p, case.scale, 0)
+        assert_attn_close(g[t], ref, f"token {t}")
+        assert np.max(np.abs(gl[t] - ref_lse)) <= 1e-3
 
 
 def _run_with_prologue(case, kp, vp, table, hint=None):
