@@ -493,7 +493,7 @@ def main():
     traffic = pmc_traffic(f"decode_{args.workload}", dec_sources)
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-                    kernel="decode attention (split-K kernel + LSE merge kernel)",
+                    kernel="decode attention (split-K kernel, last split merges)",
                     algorithmic_bytes_per_call=int(sum(attn_bytes) / wl.n_calls),
                     us_per_call=round(ms_attn * 1e3, 3))
     result = {

@@ -147,11 +147,13 @@ pkv_status pkv_append(const void* k_new, const void* v_new, const int32_t* slot,
  *   out      : device bf16 [B][n_q_heads][head_dim]
  *   lse      : device fp32 [B][n_q_heads] natural-log sum-exp, or NULL
  *   workspace: device scratch of >= pkv_decode_workspace_size(...) bytes
- *              (NULL allowed when that size is 0); its contents need no
- *              initialisation.  Calls that share a workspace must not run
- *              concurrently.
- * n_q_heads / n_kv_heads must be an integer G in [1, 16] with G * head_dim <= 2048
- * (PKV_ERR_UNSUPPORTED otherwise).  B == 0 is a no-op.
+ *              (NULL allowed when that size is 0) for the split partials; its
+ *              contents need no initialisation.
+ * The splits of a (row, kv head) count themselves in on per-device counters
+ * inside the library (the last one merges); decode calls on one device must
+ * therefore not overlap in time, whatever their workspaces.
+ * n_q_heads / n_kv_heads must be an integer G in [1, 16] with G * head_dim <= 2048,
+ * and B * n_kv_heads <= 65536 (PKV_ERR_UNSUPPORTED otherwise).  B == 0 is a no-op.
  */
 pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slots,
                            const int32_t* seq_lens, int32_t B, int32_t max_seq_len_hint,

@@ -145,6 +145,9 @@ pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slot
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "%s: scale must be finite", fn);
   if (max_seq_len_hint < 1)
     return fail(PKV_ERR_INVALID_ARG, "%s: max_seq_len_hint must be >= 1", fn);
+  if ((long)B * g.n_kv > pkv::kDecodeMaxPairs)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: B * n_kv_heads must be <= %d (got %ld)", fn,
+                pkv::kDecodeMaxPairs, (long)B * g.n_kv);
   if (B == 0) return PKV_OK;
   if (!q || !slots || !seq_lens || !k_pool || !v_pool || !out)
     return fail(PKV_ERR_INVALID_ARG, "%s: NULL tensor pointer", fn);

@@ -24,12 +24,14 @@
 // a chunk at the head_dim-128 size.
 //
 // With several splits per row the partial (o, max, sum) of each workgroup
-// goes to the workspace and a small merge kernel combines them in fixed split
-// order (bitwise deterministic).  (A last-arriving-workgroup merge inside the
-// split kernel needs an agent-scope release per workgroup, which on gfx950 is
-// an L2 write-back each; measured far slower than the second launch.)
-// Optionally the new token's K/V is appended first by the workgroup that owns
-// the last key.
+// goes to the workspace and the last workgroup of the (row, kv head) to
+// arrive merges them, in fixed split order (bitwise deterministic whichever
+// workgroup merges).  The partials are written and read with device-scope
+// relaxed atomic accesses (sc1: coherent across the XCDs' L2s), each writer
+// waits for its stores to complete before it counts itself in, and the
+// counter wraps to zero on the last arrival -- no release fence, which on
+// gfx950 would write back the whole L2 per workgroup.  Optionally the new
+// token's K/V is appended first by the workgroup that owns the last key.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -42,6 +44,13 @@ constexpr int kThreads = kDecodeWaves * 64;
 constexpr int kSegPages = 64;  // page ids staged in LDS per range segment
 constexpr int kMaxGD = 2048;   // (query heads per kv head) * head_dim, checked on the host
 constexpr int kMaxMergeWeights = 1024;  // splits * G of one (row, kv head)
+
+// Split arrival counters, one per (row, kv head) of a call (index
+// b * n_kv + hk < kDecodeMaxPairs, host-checked).  Zero at load; every call
+// leaves them zero again (the increment wraps on the last arrival), so they
+// need no clearing.  Each GPU has its own copy; decode calls on one GPU must
+// not overlap in time.
+__device__ uint32_t g_split_arrivals[kDecodeMaxPairs];
 
 // Masks the bf16 elements e >= nvalid (0..8) of an 8-element operand.
 __device__ __forceinline__ u32x4 keep_first(u32x4 v, int nvalid) {
@@ -101,14 +110,88 @@ __device__ __forceinline__ void stage_pages(const DecodeArgs& a, const int32_t* 
   }
 }
 
-// Writes this workgroup's result: the final output (single split) or its
-// unnormalised partial (o, running max in log2 units, sum) for the merge
-// kernel.  o_val(g, d), Mof(g), Lof(g) give the workgroup's values.
+// Device-scope (sc1) accesses of the split partials: coherent across the
+// XCDs' L2s without any cache write-back or invalidation.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev2(float* p, float lo, float hi) {  // p 8-byte aligned
+  const uint64_t v = (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_dev2(const float* p) {  // p 8-byte aligned
+  return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Log-sum-exp merge of the n_valid split partials of one (row, kv head), in
+// fixed split order.  s_w holds >= n_valid * G floats.
+template <int D>
+__device__ void merge_splits(const DecodeArgs& a, int b, int hk, int n_valid, float* s_w) {
+  const int G = a.G, S = a.max_splits;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const size_t pbase = ((size_t)b * a.g.n_kv + hk) * S;
+  const float* ml = a.part_ml + pbase * G * 2;
+  for (int g = w; g < G; g += nw) {
+    float M = -INFINITY;
+    for (int t = lane; t < n_valid; t += 64) {
+      const float m = load_dev(ml + (t * G + g) * 2), l = load_dev(ml + (t * G + g) * 2 + 1);
+      if (l > 0.f) M = fmaxf(M, m);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor(M, m));
+    float lsum = 0.f;
+    for (int t = lane; t < n_valid; t += 64) {
+      const float m = load_dev(ml + (t * G + g) * 2), l = load_dev(ml + (t * G + g) * 2 + 1);
+      const float f = l > 0.f ? fast_exp2(m - M) : 0.f;
+      s_w[t * G + g] = f;
+      lsum += f * l;
+    }
+    lsum = wave_sum(lsum);
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    for (int t = lane; t < n_valid; t += 64) s_w[t * G + g] *= inv;
+    if (a.lse && lane == 0)
+      a.lse[(size_t)b * a.n_q + hk * G + g] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+  constexpr int kU = 8;  // splits whose loads are in flight together
+  for (int idx = threadIdx.x; idx < G * D / 2; idx += blockDim.x) {
+    const int g = (2 * idx) / D, d = 2 * idx - g * D;
+    float o0 = 0.f, o1 = 0.f;
+    const float* po = a.part_o + (pbase * G + g) * D + d;
+    for (int t0 = 0; t0 < n_valid; t0 += kU) {
+      uint64_t v[kU];
+#pragma unroll
+      for (int j = 0; j < kU; ++j) v[j] = t0 + j < n_valid ? load_dev2(po + (size_t)(t0 + j) * G * D) : 0;
+#pragma unroll
+      for (int j = 0; j < kU; ++j) {
+        // empty partials (zero sum) have weight 0 and are never written: select them away
+        const float wt = t0 + j < n_valid ? s_w[(t0 + j) * G + g] : 0.f;
+        if (wt != 0.f) {
+          o0 += wt * __uint_as_float((uint32_t)v[j]);
+          o1 += wt * __uint_as_float((uint32_t)(v[j] >> 32));
+        }
+      }
+    }
+    a.out[((size_t)b * a.n_q + hk * G + g) * D + d] = f32_to_bf16(o0);
+    a.out[((size_t)b * a.n_q + hk * G + g) * D + d + 1] = f32_to_bf16(o1);
+  }
+}
+
+// Writes this workgroup's result: the final output when it is the row's only
+// split, else its unnormalised partial (o, running max in log2 units, sum),
+// and the last split to arrive merges all partials.  o_val(g, d), Mof(g),
+// Lof(g) give the workgroup's values; s_w is LDS free for the merge weights
+// (>= n_valid * G floats, not read by o_val / Mof / Lof).
 template <int D, class OFn, class MFn, class LFn>
-__device__ void finish(const DecodeArgs& a, int b, int hk, int s, OFn o_val, MFn Mof, LFn Lof) {
+__device__ void finish(const DecodeArgs& a, const RowRange& r, int b, int hk, int s, OFn o_val,
+                       MFn Mof, LFn Lof, float* s_w) {
   const int G = a.G;
   const int tid = threadIdx.x;
-  if (a.max_splits == 1) {
+  if (r.n_valid <= 1) {
     for (int idx = tid; idx < G * D; idx += blockDim.x) {
       const int g = idx / D, d = idx - g * D;
       const float l = Lof(g);
@@ -119,88 +202,37 @@ __device__ void finish(const DecodeArgs& a, int b, int hk, int s, OFn o_val, MFn
     return;
   }
   const size_t pbase = ((size_t)b * a.g.n_kv + hk) * a.max_splits + s;
-  for (int idx = tid; idx < G * D; idx += blockDim.x) {
-    const int g = idx / D, d = idx - g * D;
-    a.part_o[(pbase * G + g) * D + d] = o_val(g, d);
+  for (int idx = tid; idx < G * D / 2; idx += blockDim.x) {
+    const int g = (2 * idx) / D, d = 2 * idx - g * D;
+    store_dev2(a.part_o + (pbase * G + g) * D + d, o_val(g, d), o_val(g, d + 1));
   }
   for (int g = tid; g < G; g += blockDim.x) {
-    a.part_ml[(pbase * G + g) * 2] = Mof(g);
-    a.part_ml[(pbase * G + g) * 2 + 1] = Lof(g);
+    store_dev(a.part_ml + (pbase * G + g) * 2, Mof(g));
+    store_dev(a.part_ml + (pbase * G + g) * 2 + 1, Lof(g));
   }
-}
-
-// A split with nothing to do (idle row, or a split past the row's last key)
-// leaves an empty partial: max -inf, sum 0.  The merge skips it.
-__device__ __forceinline__ void empty_partial(const DecodeArgs& a, int b, int hk, int s) {
-  if (a.max_splits == 1) return;
-  const size_t pbase = ((size_t)b * a.g.n_kv + hk) * a.max_splits + s;
-  for (int g = threadIdx.x; g < a.G; g += blockDim.x) {
-    a.part_ml[(pbase * a.G + g) * 2] = -INFINITY;
-    a.part_ml[(pbase * a.G + g) * 2 + 1] = 0.f;
-  }
-}
-
-__device__ __forceinline__ void idle_output(const DecodeArgs& a, int b, int hk, int s, int D) {
-  if (a.max_splits == 1) {
-    for (int idx = threadIdx.x; idx < a.G * D; idx += blockDim.x) {
-      const int g = idx / D, d = idx - g * D;
-      a.out[((size_t)b * a.n_q + hk * a.G + g) * D + d] = 0;
-      if (a.lse && d == 0) a.lse[(size_t)b * a.n_q + hk * a.G + g] = -INFINITY;
-    }
-  } else {
-    empty_partial(a, b, hk, s);
-  }
-}
-
-// Log-sum-exp merge of the split partials of one (row, kv head), in fixed
-// split order.  Needs no row metadata: empty partials carry a zero sum.  One
-// wave per query column reduces the split maxima and sums across its lanes.
-template <int D>
-__global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
-  __shared__ float s_w[kMaxMergeWeights];
-  const int hk = blockIdx.x, b = blockIdx.y;
-  const int G = a.G, S = a.max_splits;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const size_t pbase = ((size_t)b * a.g.n_kv + hk) * S;
-  const float* ml = a.part_ml + pbase * G * 2;
-  for (int g = w; g < G; g += kDecodeWaves) {
-    float M = -INFINITY;
-    for (int t = lane; t < S; t += 64) {
-      const float2 v = *reinterpret_cast<const float2*>(ml + (t * G + g) * 2);
-      if (v.y > 0.f) M = fmaxf(M, v.x);
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor(M, m));
-    float lsum = 0.f;
-    for (int t = lane; t < S; t += 64) {
-      const float2 v = *reinterpret_cast<const float2*>(ml + (t * G + g) * 2);
-      const float f = v.y > 0.f ? fast_exp2(v.x - M) : 0.f;
-      s_w[t * G + g] = f;
-      lsum += f * v.y;
-    }
-    lsum = wave_sum(lsum);
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    for (int t = lane; t < S; t += 64) s_w[t * G + g] *= inv;
-    if (a.lse && lane == 0)
-      a.lse[(size_t)b * a.n_q + hk * G + g] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
+  __builtin_amdgcn_s_waitcnt(0);          // this thread's partial stores are complete
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);  // (and stay before the arrival below)
+  __shared__ int s_last;
+  __syncthreads();                        // ... and so are the whole workgroup's
+  if (tid == 0) {
+    // wraps to 0 on the n_valid-th arrival, ready for the next call
+    const uint32_t old = __builtin_amdgcn_atomic_inc32(g_split_arrivals + (size_t)b * a.g.n_kv + hk,
+                                                       (uint32_t)(r.n_valid - 1), __ATOMIC_RELAXED,
+                                                       "agent");
+    s_last = old == (uint32_t)(r.n_valid - 1);
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D / 4; idx += kThreads) {
-    const int g = (4 * idx) / D, d = 4 * idx - g * D;
-    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float* po = a.part_o + (pbase * G + g) * D + d;
-    // Loads are unconditional (an empty partial's o is never written and may
-    // hold anything); the select drops them, so they can all be in flight.
-#pragma unroll 8
-    for (int t = 0; t < S; ++t) {
-      const float wt = s_w[t * G + g];
-      const f32x4 v = *reinterpret_cast<const f32x4*>(po + (size_t)t * G * D);
-      o += wt != 0.f ? wt * v : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    uint2 pk;
-    pk.x = pack_bf16x2(o[0], o[1]);
-    pk.y = pack_bf16x2(o[2], o[3]);
-    *reinterpret_cast<uint2*>(a.out + ((size_t)b * a.n_q + hk * G + g) * D + d) = pk;
+  if (s_last) merge_splits<D>(a, b, hk, r.n_valid, s_w);
+}
+
+// An idle row (padding slot or empty context): split 0 writes out = 0 and
+// lse = -inf; the other splits have nothing to do.
+__device__ __forceinline__ void idle_output(const DecodeArgs& a, int b, int hk, int s, int D) {
+  if (s != 0) return;
+  for (int idx = threadIdx.x; idx < a.G * D; idx += blockDim.x) {
+    const int g = idx / D, d = idx - g * D;
+    a.out[((size_t)b * a.n_q + hk * a.G + g) * D + d] = 0;
+    if (a.lse && d == 0) a.lse[(size_t)b * a.n_q + hk * a.G + g] = -INFINITY;
   }
 }
 
@@ -209,6 +241,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_keysplit_kernel(DecodeArgs a) {
   extern __shared__ float s_o[];                  // [wave][G][D] (dynamic: NW * G * D)
+  __shared__ float s_w[kMaxMergeWeights];         // merge weights (last split of a row)
   __shared__ int s_pg[kSegPages];
   __shared__ float s_ml[2 * NW * 16];             // [wave][16] max, then sum
   __shared__ float s_red[NW * 16 + 32];
@@ -218,13 +251,10 @@ __global__ __launch_bounds__(NW * 64) void decode_keysplit_kernel(DecodeArgs a) 
   const int G = a.G;
   const RowRange r = row_range(a, b, s);
   if (r.idle) {
-    if (s == 0 || a.max_splits > 1) idle_output(a, b, hk, s, D);
+    idle_output(a, b, hk, s, D);
     return;
   }
-  if (r.start >= r.L) {
-    empty_partial(a, b, hk, s);
-    return;
-  }
+  if (s >= r.n_valid) return;  // past the row's last key: not counted by the merge
   if (a.k_new && r.end == r.L) append_new_token(a, r, b, hk, D);
 
   const int ps = a.g.page_size, log2ps = a.g.log2ps;
@@ -357,7 +387,7 @@ __global__ __launch_bounds__(NW * 64) void decode_keysplit_kernel(DecodeArgs a) 
   };
   auto Mof = [&](int g) { return s_red[NW * 16 + g]; };
   auto Lof = [&](int g) { return s_red[NW * 16 + 16 + g]; };
-  finish<D>(a, b, hk, s, o_val, Mof, Lof);
+  finish<D>(a, r, b, hk, s, o_val, Mof, Lof, s_w);
 }
 
 // ---------------------------------------------------------------------------
@@ -368,6 +398,7 @@ __global__ __launch_bounds__(kThreads) void decode_dimsplit_kernel(DecodeArgs a)
   __shared__ int s_pg[kSegPages];
   __shared__ f32x4 s_part[2][kDecodeWaves][2][64];  // [buffer][wave][rg][lane]
   __shared__ float s_o[kMaxGD];                     // [G][D] final unnormalised output
+  __shared__ float s_w[kMaxMergeWeights];           // merge weights (last split of a row)
   __shared__ float s_ml[32];
   const int s = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -375,13 +406,10 @@ __global__ __launch_bounds__(kThreads) void decode_dimsplit_kernel(DecodeArgs a)
   const int G = a.G;
   const RowRange r = row_range(a, b, s);
   if (r.idle) {
-    if (s == 0 || a.max_splits > 1) idle_output(a, b, hk, s, D);
+    idle_output(a, b, hk, s, D);
     return;
   }
-  if (r.start >= r.L) {
-    empty_partial(a, b, hk, s);
-    return;
-  }
+  if (s >= r.n_valid) return;  // past the row's last key: not counted by the merge
   if (a.k_new && r.end == r.L) append_new_token(a, r, b, hk, D);
 
   const int dw0 = w * DW;
@@ -496,7 +524,7 @@ __global__ __launch_bounds__(kThreads) void decode_dimsplit_kernel(DecodeArgs a)
   auto o_val = [&](int g, int d) { return s_o[g * D + d]; };
   auto Mof = [&](int g) { return s_ml[g]; };
   auto Lof = [&](int g) { return s_ml[16 + g]; };
-  finish<D>(a, b, hk, s, o_val, Mof, Lof);
+  finish<D>(a, r, b, hk, s, o_val, Mof, Lof, s_w);
 }
 
 template <int D>
@@ -511,9 +539,6 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t st) {
                          (size_t)kDecodeWaves * a.G * D * sizeof(float), st, a);
   } else
     hipLaunchKernelGGL((decode_dimsplit_kernel<D>), grid, dim3(kThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.max_splits == 1) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.g.n_kv, a.B), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

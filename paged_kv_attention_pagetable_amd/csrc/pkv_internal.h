@@ -121,6 +121,8 @@ struct DecodePlan {
   size_t ws_bytes;
   size_t part_o_floats;  // partial outputs first, then the (max, sum) pairs
 };
+// Largest B * n_kv of a decode call (split arrival counters on the device).
+constexpr int kDecodeMaxPairs = 1 << 16;
 DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_hint,
                        int window);
 
