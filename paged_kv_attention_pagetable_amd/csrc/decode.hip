@@ -287,9 +287,10 @@ __global__ __launch_bounds__(NW * 64) void decode_keysplit_kernel(DecodeArgs a) 
         qreg[c] = qc < G ? v : u32x4{0, 0, 0, 0};
       }
     }
-    for (int t0 = seg0 + 32 * w; t0 < seg1; t0 += 32 * NW) {
-      // ---- issue the chunk's K and V^T loads together
-      u32x4 kop[2][D / 32];
+    // The K/V operands of a wave's chunk (32 keys at t0): K rows of MFMA rows
+    // and V^T rows, 16-byte loads straight into registers; keys >= seg1
+    // (unmapped or past the range) load as zero.
+    auto load_chunk = [&](int t0, u32x4 (&kop)[2][D / 32], u32x4 (&vop)[D / 16]) {
 #pragma unroll
       for (int rg = 0; rg < 2; ++rg) {
         const int tk = t0 + 8 * (qc >> 2) + 4 * rg + (qc & 3);
@@ -302,12 +303,26 @@ __global__ __launch_bounds__(NW * 64) void decode_keysplit_kernel(DecodeArgs a) 
       const int vpage = tv < seg1 ? s_pg[(tv >> log2ps) - p0] : -1;
       const int nvalid = seg1 - tv;
       const bf16_t* vp = vbase + (size_t)max(vpage, 0) * page_stride + (size_t)qc * ps + (tv & (ps - 1));
-      u32x4 vop[D / 16];
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
         vop[dt] = vpage >= 0 ? load16(vp + (size_t)16 * dt * ps) : u32x4{0, 0, 0, 0};
         if (nvalid < 8) vop[dt] = keep_first(vop[dt], nvalid);
       }
+    };
+    // Register double buffer: the next chunk's loads are in flight while
+    // this chunk is computed.
+    u32x4 kop_n[2][D / 32], vop_n[D / 16];
+    if (seg0 + 32 * w < seg1) load_chunk(seg0 + 32 * w, kop_n, vop_n);
+    for (int t0 = seg0 + 32 * w; t0 < seg1; t0 += 32 * NW) {
+      u32x4 kop[2][D / 32], vop[D / 16];
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) kop[rg][c] = kop_n[rg][c];
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) vop[dt] = vop_n[dt];
+      if (t0 + 32 * NW < seg1) load_chunk(t0 + 32 * NW, kop_n, vop_n);
+      const int tv = t0 + 8 * quad;
       // ---- S^T = K Q^T; MFMA rg row m holds key 8*(m/4) + 4*rg + m%4
       f32x4 S[2];
 #pragma unroll
