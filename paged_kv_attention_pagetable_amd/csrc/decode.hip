@@ -239,7 +239,8 @@ __device__ __forceinline__ void idle_output(const DecodeArgs& a, int b, int hk, 
 // ---------------------------------------------------------------------------
 // head_dim <= 128: key split across the NW waves of the workgroup.
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_keysplit_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_keysplit_kernel(DecodeArgs a) {
   extern __shared__ float s_o[];                  // [wave][G][D] (dynamic: NW * G * D)
   __shared__ float s_w[kMaxMergeWeights];         // merge weights (last split of a row)
   __shared__ int s_pg[kSegPages];
@@ -297,7 +298,10 @@ __global__ __launch_bounds__(NW * 64) void decode_keysplit_kernel(DecodeArgs a) 
         const int page = tk < seg1 ? s_pg[(tk >> log2ps) - p0] : -1;
         const bf16_t* kp = kbase + (size_t)max(page, 0) * page_stride + (size_t)(tk & (ps - 1)) * D + 8 * quad;
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) kop[rg][c] = page >= 0 ? load16(kp + 32 * c) : u32x4{0, 0, 0, 0};
+        for (int c = 0; c < D / 32; ++c) {
+          const u32x4 v = load16(kp + 32 * c);  // unconditional: the wait counts stay exact
+          kop[rg][c] = page >= 0 ? v : u32x4{0, 0, 0, 0};
+        }
       }
       const int tv = t0 + 8 * quad;
       const int vpage = tv < seg1 ? s_pg[(tv >> log2ps) - p0] : -1;
@@ -305,8 +309,8 @@ __global__ __launch_bounds__(NW * 64) void decode_keysplit_kernel(DecodeArgs a) 
       const bf16_t* vp = vbase + (size_t)max(vpage, 0) * page_stride + (size_t)qc * ps + (tv & (ps - 1));
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
-        vop[dt] = vpage >= 0 ? load16(vp + (size_t)16 * dt * ps) : u32x4{0, 0, 0, 0};
-        if (nvalid < 8) vop[dt] = keep_first(vop[dt], nvalid);
+        const u32x4 v = load16(vp + (size_t)16 * dt * ps);
+        vop[dt] = vpage >= 0 ? (nvalid < 8 ? keep_first(v, nvalid) : v) : u32x4{0, 0, 0, 0};
       }
     };
     // Register double buffer: the next chunk's loads are in flight while
@@ -465,7 +469,10 @@ __global__ __launch_bounds__(kThreads) void decode_dimsplit_kernel(DecodeArgs a)
         const int page = tk < seg1 ? s_pg[(tk >> log2ps) - p0] : -1;
         const bf16_t* kp = kbase + (size_t)max(page, 0) * page_stride + (size_t)(tk & (ps - 1)) * D + 8 * quad;
 #pragma unroll
-        for (int c = 0; c < DW / 32; ++c) kop[rg][c] = page >= 0 ? load16(kp + 32 * c) : u32x4{0, 0, 0, 0};
+        for (int c = 0; c < DW / 32; ++c) {
+          const u32x4 v = load16(kp + 32 * c);  // unconditional: the wait counts stay exact
+          kop[rg][c] = page >= 0 ? v : u32x4{0, 0, 0, 0};
+        }
       }
       const int tv = t0 + 8 * quad;
       const int vpage = tv < seg1 ? s_pg[(tv >> log2ps) - p0] : -1;
@@ -474,8 +481,8 @@ __global__ __launch_bounds__(kThreads) void decode_dimsplit_kernel(DecodeArgs a)
       u32x4 vop[DW / 16];
 #pragma unroll
       for (int dt = 0; dt < DW / 16; ++dt) {
-        vop[dt] = vpage >= 0 ? load16(vp + (size_t)16 * dt * ps) : u32x4{0, 0, 0, 0};
-        if (nvalid < 8) vop[dt] = keep_first(vop[dt], nvalid);
+        const u32x4 v = load16(vp + (size_t)16 * dt * ps);
+        vop[dt] = vpage >= 0 ? (nvalid < 8 ? keep_first(v, nvalid) : v) : u32x4{0, 0, 0, 0};
       }
 #pragma unroll
       for (int rg = 0; rg < 2; ++rg) {
