@@ -34,12 +34,15 @@
  *
  * Cache layout (one K pool and one V pool per layer, same page geometry):
  *   K pool: bf16 [n_pages][n_kv_heads][page_size][head_dim]   (token rows)
- *   V pool: bf16 [n_pages][n_kv_heads][head_dim][page_size]   (d-major rows)
+ *   V pool: bf16 [n_pages][n_kv_heads][page_size/gs][head_dim][gs],
+ *           gs = min(page_size, 32): the page's rows in groups of 32 keys,
+ *           each group d-major (element (d, row) at group row/gs, [d][row%gs])
  *   The pages' cache is a single (1, H, n_pages*page_size, D) buffer per K/V
  *   ([continuous-batching compare] flex_paged_attention.py, PagedKVCache);
  *   here pages are the outer dimension so one (page, head) block is contiguous,
- *   and V is stored d-major inside a page so the P.V contraction can feed the
- *   matrix cores straight from memory.
+ *   and V is stored d-major inside 32-key groups so the P.V contraction can
+ *   feed the matrix cores straight from memory, with one wave's 32 keys of V
+ *   one contiguous block.  For page_size <= 32 this is plain d-major pages.
  *
  * Page table ([continuous-batching compare] flex_paged_attention.py, PageTable):
  *   int32 [max_slots][pages_per_slot], entry = physical page of

@@ -8,7 +8,9 @@ one ``(1, H, n_pages*page_size, D)`` buffer per K and V, see
 ``PagedKVCache.__init__``):
 
 * K pool: bf16 ``[n_pages][n_kv][page_size][D]``  (token rows, D contiguous)
-* V pool: bf16 ``[n_pages][n_kv][D][page_size]``  (d-major within a page)
+* V pool: bf16 ``[n_pages][n_kv][page_size/gs][D][gs]``, ``gs = min(page_size,
+  32)``: a page's rows in groups of ``gs`` consecutive keys, each group stored
+  d-major; element (d, row) is ``v_pool[page, head, row // gs, d, row % gs]``
 * page table: int ``[max_slots][pages_per_slot]``; entry ``-1`` = unmapped;
   slot 0 is the reserved no-op slot and page 0 the reserved page.
 
@@ -87,6 +89,7 @@ def append(k_pool, v_pool, table, k_new, v_new, slot, pos) -> None:
     ``page_table[slot, pos // page_size]``, row ``pos % page_size``.
     """
     ps = k_pool.shape[2]
+    gs = v_pool.shape[4]
     for t in range(len(slot)):
         s = int(slot[t])
         if s == 0:
@@ -95,18 +98,20 @@ def append(k_pool, v_pool, table, k_new, v_new, slot, pos) -> None:
         phys = physical_page(table, s, p, ps)
         row = p % ps
         k_pool[phys, :, row, :] = k_new[t]
-        v_pool[phys, :, :, row] = v_new[t]
+        v_pool[phys, :, row // gs, :, row % gs] = v_new[t]
 
 
 def gather_kv(k_pool, v_pool, table, slot: int, length: int):
     """Dense float64 ``K, V [length][n_kv][D]`` of ``slot``'s logical tokens."""
     n_kv, ps, D = k_pool.shape[1], k_pool.shape[2], k_pool.shape[3]
+    gs = v_pool.shape[4]
     K = np.empty((length, n_kv, D), dtype=np.float64)
     V = np.empty((length, n_kv, D), dtype=np.float64)
     for j in range(length):
         phys = physical_page(table, slot, j, ps)
         K[j] = bf16_bits_to_f64(k_pool[phys, :, j % ps, :])
-        V[j] = bf16_bits_to_f64(v_pool[phys, :, :, j % ps])
+        row = j % ps
+        V[j] = bf16_bits_to_f64(v_pool[phys, :, row // gs, :, row % gs])
     return K, V
 
 

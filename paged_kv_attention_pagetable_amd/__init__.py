@@ -8,7 +8,9 @@ not built, every call raises.
 Tensors (all on the same HIP device, contiguous):
 
 * ``k_pool``: bf16 ``[n_pages, n_kv, page_size, head_dim]``
-* ``v_pool``: bf16 ``[n_pages, n_kv, head_dim, page_size]`` (d-major pages)
+* ``v_pool``: bf16 ``[n_pages, n_kv, page_size // gs, head_dim, gs]`` with
+  ``gs = min(page_size, 32)``: each page's rows in groups of 32 keys, each
+  group d-major (see ``v_pool_shape``)
 * ``table``:  int32 ``[max_slots, pages_per_slot]``, -1 = unmapped, slot 0
   reserved
 """
@@ -24,7 +26,7 @@ from . import _lib
 from ._lib import CacheDesc, PageTableRef, Prologue, PkvError, check, lib
 
 __all__ = ["append", "attn_decode", "attn_prefill", "decode_workspace_size", "rope_table",
-           "new_pools", "new_decode_workspace", "PageAllocator", "PkvError", "lib"]
+           "new_pools", "v_pool_shape", "new_decode_workspace", "PageAllocator", "PkvError", "lib"]
 
 
 def _ptr(t):
@@ -55,12 +57,12 @@ def _cache(k_pool, v_pool, table):
     _bits16(k_pool, "k_pool")
     _bits16(v_pool, "v_pool")
     _i32(table, "table")
-    if k_pool.dim() != 4 or v_pool.dim() != 4:
-        raise ValueError("pools must be 4-D")
+    if k_pool.dim() != 4:
+        raise ValueError("k_pool must be 4-D [n_pages, n_kv, page_size, head_dim]")
     n_pages, n_kv, ps, D = k_pool.shape
-    if tuple(v_pool.shape) != (n_pages, n_kv, D, ps):
-        raise ValueError(f"v_pool must be [n_pages, n_kv, head_dim, page_size] = "
-                         f"{(n_pages, n_kv, D, ps)}, got {tuple(v_pool.shape)}")
+    if tuple(v_pool.shape) != v_pool_shape(n_pages, n_kv, ps, D):
+        raise ValueError(f"v_pool must be [n_pages, n_kv, page_size // gs, head_dim, gs] = "
+                         f"{v_pool_shape(n_pages, n_kv, ps, D)}, got {tuple(v_pool.shape)}")
     if table.dim() != 2:
         raise ValueError("table must be [max_slots, pages_per_slot]")
     cd = CacheDesc(n_pages, ps, n_kv, D)
@@ -68,10 +70,17 @@ def _cache(k_pool, v_pool, table):
     return cd, pt
 
 
+def v_pool_shape(n_pages, n_kv, page_size, head_dim):
+    """Shape of the V pool: 32-key groups of each page, d-major inside a group."""
+    gs = min(page_size, 32)
+    return (n_pages, n_kv, page_size // gs, head_dim, gs)
+
+
 def new_pools(n_pages, n_kv, page_size, head_dim, device="cuda", fill=None):
     """Allocate a K and a V pool (bf16) in the library's layout."""
     k = torch.empty((n_pages, n_kv, page_size, head_dim), dtype=torch.bfloat16, device=device)
-    v = torch.empty((n_pages, n_kv, head_dim, page_size), dtype=torch.bfloat16, device=device)
+    v = torch.empty(v_pool_shape(n_pages, n_kv, page_size, head_dim), dtype=torch.bfloat16,
+                    device=device)
     if fill is not None:
         k.view(torch.int16).fill_(fill)
         v.view(torch.int16).fill_(fill)

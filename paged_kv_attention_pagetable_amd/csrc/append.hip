@@ -1,9 +1,10 @@
 // Append kernel: scatter new K/V rows into the paged pools (bit copy).
 //
 // K goes to the token-major K pool with one 16-byte store per 8 dims.  V goes
-// to the d-major V pool: a workgroup stages 64 consecutive tokens of one kv
-// head in LDS and writes each V^T row segment with lanes on consecutive
-// tokens, so runs of tokens that share a page become contiguous stores.
+// to the V pool, d-major within 32-key groups: a workgroup stages 64
+// consecutive tokens of one kv head in LDS and writes each V^T row segment
+// with lanes on consecutive tokens, so runs of tokens that share a page (and
+// a key group) become contiguous stores.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     if (tt >= nt) continue;
     const int page = s_page[tt];
     if (page < 0) continue;
-    a.vpool[(size_t)page * page_stride + h * blk + (size_t)d * ps + s_row[tt]] = s_v[tt][d];
+    a.vpool[(size_t)page * page_stride + h * blk + v_elem_offset(d, s_row[tt], D, a.g.log2ps)] = s_v[tt][d];
   }
 }
 

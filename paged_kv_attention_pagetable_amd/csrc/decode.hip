@@ -9,8 +9,9 @@
 //   S^T[32 keys][16 q]  = K[32][D] . Q^T[D][16]
 //   O^T[D][16 q]       += V^T[D][32 keys] . P^T[32][16]
 //
-// K rows come from the token-major K pool and V^T rows from the d-major V
-// pool as 16-byte loads straight into MFMA operand registers; a lane's 8 key
+// K rows come from the token-major K pool and V^T rows from the V pool
+// (d-major within 32-key groups, so one wave's 32 keys of V are one
+// contiguous block) as 16-byte loads straight into MFMA operand registers; a lane's 8 key
 // scores land exactly in its P^T k-slots, so no LDS round trip is needed for
 // P.  The physical page ids of the workgroup's range are read once into LDS,
 // so no page-table load sits on a chunk's critical path, and each chunk's K
@@ -98,7 +99,8 @@ __device__ __forceinline__ void append_new_token(const DecodeArgs& a, const RowR
   const size_t src = ((size_t)b * a.g.n_kv + hk) * D;
   for (int i = threadIdx.x; i < D / 8; i += blockDim.x)
     store16(a.kpool_w + dst + (size_t)row * D + 8 * i, load16(a.k_new + src + 8 * i));
-  for (int d = threadIdx.x; d < D; d += blockDim.x) a.vpool_w[dst + (size_t)d * ps + row] = a.v_new[src + d];
+  for (int d = threadIdx.x; d < D; d += blockDim.x)
+    a.vpool_w[dst + v_elem_offset(d, row, D, a.g.log2ps)] = a.v_new[src + d];
 }
 
 // Stages the page ids of logical pages [p0, p0 + n) of the row into LDS.
@@ -262,6 +264,7 @@ void decode_keysplit_kernel(DecodeArgs a) {
   const int32_t* trow = a.pt.table + (size_t)r.slot * a.pt.pps;
   const size_t blk = (size_t)ps * D;
   const size_t page_stride = (size_t)a.g.n_kv * blk;
+  const int lgv = min(log2ps, kLog2VGroup);  // log2 of the V key-group size
   const bf16_t* kbase = a.kpool + hk * blk;
   const bf16_t* vbase = a.vpool + hk * blk;
 
@@ -306,10 +309,11 @@ void decode_keysplit_kernel(DecodeArgs a) {
       const int tv = t0 + 8 * quad;
       const int vpage = tv < seg1 ? s_pg[(tv >> log2ps) - p0] : -1;
       const int nvalid = seg1 - tv;
-      const bf16_t* vp = vbase + (size_t)max(vpage, 0) * page_stride + (size_t)qc * ps + (tv & (ps - 1));
+      // V^T row d = 16*dt + qc, keys tv .. tv+7 (inside one key group)
+      const bf16_t* vp = vbase + (size_t)max(vpage, 0) * page_stride + v_elem_offset(qc, tv & (ps - 1), D, log2ps);
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
-        const u32x4 v = load16(vp + (size_t)16 * dt * ps);
+        const u32x4 v = load16(vp + ((size_t)16 * dt << lgv));
         vop[dt] = vpage >= 0 ? (nvalid < 8 ? keep_first(v, nvalid) : v) : u32x4{0, 0, 0, 0};
       }
     };
@@ -438,8 +442,9 @@ __global__ __launch_bounds__(kThreads) void decode_dimsplit_kernel(DecodeArgs a)
   const int32_t* trow = a.pt.table + (size_t)r.slot * a.pt.pps;
   const size_t blk = (size_t)ps * D;
   const size_t page_stride = (size_t)a.g.n_kv * blk;
+  const int lgv = min(log2ps, kLog2VGroup);  // log2 of the V key-group size
   const bf16_t* kbase = a.kpool + hk * blk + dw0;
-  const bf16_t* vbase = a.vpool + hk * blk + (size_t)dw0 * ps;
+  const bf16_t* vbase = a.vpool + hk * blk;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 acc[DW / 16];
@@ -477,11 +482,13 @@ __global__ __launch_bounds__(kThreads) void decode_dimsplit_kernel(DecodeArgs a)
       const int tv = t0 + 8 * quad;
       const int vpage = tv < seg1 ? s_pg[(tv >> log2ps) - p0] : -1;
       const int nvalid = seg1 - tv;
-      const bf16_t* vp = vbase + (size_t)max(vpage, 0) * page_stride + (size_t)qc * ps + (tv & (ps - 1));
+      // V^T row d = dw0 + 16*dt + qc, keys tv .. tv+7 (inside one key group)
+      const bf16_t* vp =
+          vbase + (size_t)max(vpage, 0) * page_stride + v_elem_offset(dw0 + qc, tv & (ps - 1), D, log2ps);
       u32x4 vop[DW / 16];
 #pragma unroll
       for (int dt = 0; dt < DW / 16; ++dt) {
-        const u32x4 v = load16(vp + (size_t)16 * dt * ps);
+        const u32x4 v = load16(vp + ((size_t)16 * dt << lgv));
         vop[dt] = vpage >= 0 ? (nvalid < 8 ? keep_first(v, nvalid) : v) : u32x4{0, 0, 0, 0};
       }
 #pragma unroll

@@ -20,6 +20,20 @@ struct PoolGeom {
   int head_dim;
 };
 
+// V pool block of one (page, kv head): its rows are split into groups of
+// kVGroup consecutive keys (the whole page when page_size is smaller), and
+// each group is stored d-major: element (d, row) at
+// ((row / gs) * head_dim + d) * gs + row % gs, gs = min(page_size, kVGroup).
+// A 32-key group of one dim is 64 contiguous bytes and a whole group is one
+// contiguous head_dim * 64-byte block.
+constexpr int kVGroup = 32;
+constexpr int kLog2VGroup = 5;
+
+__host__ __device__ inline size_t v_elem_offset(int d, int row, int head_dim, int log2ps) {
+  const int lg = log2ps < kLog2VGroup ? log2ps : kLog2VGroup;
+  return (((size_t)(row >> lg) * head_dim + d) << lg) + (row & ((1 << lg) - 1));
+}
+
 struct TableRef {
   const int32_t* table;
   int max_slots;

@@ -105,10 +105,11 @@ struct LaneConst {
 };
 
 // Source byte offsets of copy k of wave w for lane `lane`, relative to the
-// chunk's first key in its page.  The copy fills tile bytes m*1024 ..
-// m*1024+1023 (m = w*dpw + k), lane i the 16 bytes at +16*i.  K: tile row r
-// slot s holds dims 8*(s ^ k_swz(r)) ..  V^T: row d slot s holds keys
-// 8*(s ^ v_swz(d)) .. (V pages are d-major: element (d, key) at d*ps + key).
+// chunk's first key in its page (K) or to the chunk's first 32-key group of
+// V (page_size >= 64).  The copy fills tile bytes m*1024 .. m*1024+1023
+// (m = w*dpw + k), lane i the 16 bytes at +16*i.  K: tile row r slot s holds
+// dims 8*(s ^ k_swz(r)) ..  V^T: row d slot s holds keys 8*g .. 8*g+7 of the
+// chunk, g = s ^ v_swz(d): key group g/4, dim d, keys 8*(g%4) .. within it.
 // Recomputed at each use: a few ALU ops are cheaper than registers held
 // across the chunk math.
 template <int D>
@@ -118,10 +119,10 @@ __device__ __forceinline__ uint32_t dma_k_off(int k, int lane, int w) {
   return 2 * (r * D + 8 * (sk ^ k_swz<D>(r)));
 }
 template <int D>
-__device__ __forceinline__ uint32_t dma_v_off(int k, int lane, int w, int ps) {
+__device__ __forceinline__ uint32_t dma_v_off(int k, int lane, int w) {
   const int o = (w * dma_per_wave<D>() + k) * 1024 + 16 * lane;
-  const int d = o >> 7, sv = (o >> 4) & 7;
-  return 2 * (d * ps + 8 * (sv ^ v_swz(d)));
+  const int d = o >> 7, g = ((o >> 4) & 7) ^ v_swz(d);
+  return 2 * ((((g >> 2) * D + d) << kLog2VGroup) + 8 * (g & 3));
 }
 
 template <int D>
@@ -257,7 +258,7 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const Item& it,
     const size_t base = (size_t)page * page_stride;
     const int in_pg = j0 & (ps - 1);
     const uint8_t* ks = reinterpret_cast<const uint8_t*>(kbase + base + (size_t)in_pg * D);
-    const uint8_t* vs = reinterpret_cast<const uint8_t*>(vbase + base + in_pg);
+    const uint8_t* vs = reinterpret_cast<const uint8_t*>(vbase + base + (size_t)in_pg * D);  // group in_pg/32
 #pragma unroll
     for (int k = 0; k < dma_per_wave<D>(); ++k)
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const bf16_t*>(ks + dma_k_off<D>(k, lane, w)),
@@ -265,7 +266,7 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const Item& it,
                                        16, 0, 0);
 #pragma unroll
     for (int k = 0; k < dma_per_wave<D>(); ++k)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const bf16_t*>(vs + dma_v_off<D>(k, lane, w, ps)),
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const bf16_t*>(vs + dma_v_off<D>(k, lane, w)),
                                        (lds_void_ptr)(tV + (w * dma_per_wave<D>() + k) * 1024),
                                        16, 0, 0);
     return;
@@ -289,7 +290,7 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const Item& it,
     const int j = j0 + 8 * g;
     const int pgv = s_pg[min((j >> log2ps) - it.pg0, it.n_pg - 1)];
     const int page = j < it.kv_hi ? max(pgv, 0) : 0;
-    const bf16_t* src = vbase + (size_t)page * page_stride + (size_t)d * ps + (j & (ps - 1));
+    const bf16_t* src = vbase + (size_t)page * page_stride + v_elem_offset(d, j & (ps - 1), D, log2ps);
     __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(tV + (w * dma_per_wave<D>() + k) * 1024), 16, 0, 0);
   }
 }

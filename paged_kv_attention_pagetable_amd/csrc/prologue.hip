@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
     if (tt >= nt) continue;
     const int page = s_page[tt];
     if (page < 0 || s_pos[tt] < 0) continue;
-    a.vpool[(size_t)page * page_stride + h * blk + (size_t)d * ps + s_row[tt]] = s_v[tt][d];
+    a.vpool[(size_t)page * page_stride + h * blk + v_elem_offset(d, s_row[tt], D, a.g.log2ps)] = s_v[tt][d];
   }
 }
 

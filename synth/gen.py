@@ -10,6 +10,8 @@ import numpy as np
 # 0xFFFF is a bf16 NaN: any stray read of an unwritten row, of page 0 or of a
 # page no slot owns shows up as NaN in an output.
 SENTINEL_BITS = np.uint16(0xFFFF)
+# V pools store each page's rows in groups of this many keys (storage shape only)
+V_KEY_GROUP = 32
 
 CONFIGS = {
     "tiny": dict(index=0, n_q=4, n_kv=2, head_dim=64, page_size=16, lengths=(37, 50),
@@ -127,7 +129,8 @@ class DecodeCase:
 
     def empty_pools(self):
         shape_k = (self.n_pages, self.n_kv, self.page_size, self.head_dim)
-        shape_v = (self.n_pages, self.n_kv, self.head_dim, self.page_size)
+        gs = min(self.page_size, V_KEY_GROUP)
+        shape_v = (self.n_pages, self.n_kv, self.page_size // gs, self.head_dim, gs)
         return (np.full(shape_k, SENTINEL_BITS, dtype=np.uint16),
                 np.full(shape_v, SENTINEL_BITS, dtype=np.uint16))
 
@@ -231,7 +234,8 @@ class PrefillCase:
 
     def empty_pools(self):
         shape_k = (self.n_pages, self.n_kv, self.page_size, self.head_dim)
-        shape_v = (self.n_pages, self.n_kv, self.head_dim, self.page_size)
+        gs = min(self.page_size, V_KEY_GROUP)
+        shape_v = (self.n_pages, self.n_kv, self.page_size // gs, self.head_dim, gs)
         return (np.full(shape_k, SENTINEL_BITS, dtype=np.uint16),
                 np.full(shape_v, SENTINEL_BITS, dtype=np.uint16))
 

@@ -66,7 +66,7 @@ def test_append_places_rows_at_golden_addresses_and_nowhere_else():
     table = np.array(g["table"], dtype=np.int32)
     ps, n_kv, D = g["page_size"], 2, 8
     kp = np.full((8, n_kv, ps, D), SENTINEL_BITS, np.uint16)
-    vp = np.full((8, n_kv, D, ps), SENTINEL_BITS, np.uint16)
+    vp = np.full((8, n_kv, 1, D, ps), SENTINEL_BITS, np.uint16)   # page_size 4: one key group
     T = len(g["cases"])
     rng = np.random.default_rng(0)
     kn = rng.integers(0, 0x7F00, size=(T, n_kv, D)).astype(np.uint16)
@@ -81,18 +81,45 @@ def test_append_places_rows_at_golden_addresses_and_nowhere_else():
         for h in range(n_kv):
             for d in range(D):
                 assert kp[P, h, r, d] == kn[t, h, d]
-                assert vp[P, h, d, r] == vn[t, h, d]     # V pool is d-major
+                assert vp[P, h, 0, d, r] == vn[t, h, d]     # d-major inside the group
                 touched_k[P, h, r, d] = True
-                touched_v[P, h, d, r] = True
+                touched_v[P, h, 0, d, r] = True
     assert np.all(kp[~touched_k] == SENTINEL_BITS)
     assert np.all(vp[~touched_v] == SENTINEL_BITS)
+
+
+def test_append_v_key_groups_of_32():
+    """V rows of a 64-key page land in two 32-key groups, each d-major.
+
+    Flat offsets inside the (page, head) block, worked by hand from the
+    layout: element (d, row) sits at ((row // 32) * D + d) * 32 + row % 32
+    (D = 4): row 0 dim 0 -> 0, row 31 dim 3 -> 127, row 32 dim 0 -> 128,
+    row 33 dim 2 -> 193, row 63 dim 1 -> 191.
+    """
+    ps, D = 64, 4
+    table = np.array([[0], [2]], np.int32)
+    kp = np.full((3, 1, ps, D), SENTINEL_BITS, np.uint16)
+    vp = np.full((3, 1, 2, D, 32), SENTINEL_BITS, np.uint16)
+    rows = np.array([0, 31, 32, 33, 63], np.int32)
+    vn = (np.arange(5 * D, dtype=np.uint16) + 1).reshape(5, 1, D)
+    oracle.append(kp, vp, table, vn, vn, np.ones(5, np.int32), rows)
+    flat = vp[2, 0].reshape(-1)
+    expect = {(0, 0): 0, (1, 3): 127, (2, 0): 128, (3, 2): 193, (4, 1): 191}
+    for (t, d), off in expect.items():
+        assert flat[off] == vn[t, 0, d]
+    assert np.count_nonzero(flat != SENTINEL_BITS) == 5 * D
+    assert np.all(vp[:2] == SENTINEL_BITS)
+    # and the gather reads them back at their logical positions
+    K, V = oracle.gather_kv(kp, vp, table, 1, 64)
+    for t, r in enumerate(rows):
+        assert np.array_equal(V[r, 0], oracle.bf16_bits_to_f64(vn[t, 0]))
 
 
 def test_append_skips_slot_zero():
     table = np.zeros((2, 2), np.int32)
     table[1] = [1, 2]
     kp = np.full((3, 1, 4, 2), SENTINEL_BITS, np.uint16)
-    vp = np.full((3, 1, 2, 4), SENTINEL_BITS, np.uint16)
+    vp = np.full((3, 1, 1, 2, 4), SENTINEL_BITS, np.uint16)
     kn = np.ones((2, 1, 2), np.uint16)
     oracle.append(kp, vp, table, kn, kn, np.array([0, 0], np.int32), np.array([0, 5], np.int32))
     assert np.all(kp == SENTINEL_BITS) and np.all(vp == SENTINEL_BITS)
