@@ -44,7 +44,7 @@ constexpr int kDecodeWaves = 4;
 constexpr int kThreads = kDecodeWaves * 64;
 constexpr int kSegPages = 64;  // page ids staged in LDS per range segment
 constexpr int kMaxGD = 2048;   // (query heads per kv head) * head_dim, checked on the host
-constexpr int kMaxMergeWeights = 1024;  // splits * G of one (row, kv head)
+constexpr int kMaxMergeUnits = 1024;  // cap on splits * G of one (row, kv head): bounds one merge
 
 // Split arrival counters, one per (row, kv head) of a call (index
 // b * n_kv + hk < kDecodeMaxPairs, host-checked).  Zero at load; every call
@@ -130,67 +130,68 @@ __device__ __forceinline__ uint64_t load_dev2(const float* p) {  // p 8-byte ali
 }
 
 // Log-sum-exp merge of the n_valid split partials of one (row, kv head), in
-// fixed split order.  s_w holds >= n_valid * G floats.
+// fixed split order (bitwise deterministic whichever workgroup merges).  One
+// pass: each thread owns two output dims of one query head and issues the
+// (max, sum) pair and the partial o of up to kU splits together, merging them
+// online against a running maximum, so the whole merge costs one memory round
+// trip per kU splits.
 template <int D>
-__device__ void merge_splits(const DecodeArgs& a, int b, int hk, int n_valid, float* s_w) {
+__device__ void merge_splits(const DecodeArgs& a, int b, int hk, int n_valid) {
   const int G = a.G, S = a.max_splits;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const size_t pbase = ((size_t)b * a.g.n_kv + hk) * S;
   const float* ml = a.part_ml + pbase * G * 2;
-  for (int g = w; g < G; g += nw) {
-    float M = -INFINITY;
-    for (int t = lane; t < n_valid; t += 64) {
-      const float m = load_dev(ml + (t * G + g) * 2), l = load_dev(ml + (t * G + g) * 2 + 1);
-      if (l > 0.f) M = fmaxf(M, m);
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor(M, m));
-    float lsum = 0.f;
-    for (int t = lane; t < n_valid; t += 64) {
-      const float m = load_dev(ml + (t * G + g) * 2), l = load_dev(ml + (t * G + g) * 2 + 1);
-      const float f = l > 0.f ? fast_exp2(m - M) : 0.f;
-      s_w[t * G + g] = f;
-      lsum += f * l;
-    }
-    lsum = wave_sum(lsum);
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    for (int t = lane; t < n_valid; t += 64) s_w[t * G + g] *= inv;
-    if (a.lse && lane == 0)
-      a.lse[(size_t)b * a.n_q + hk * G + g] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
-  }
-  __syncthreads();
   constexpr int kU = 8;  // splits whose loads are in flight together
   for (int idx = threadIdx.x; idx < G * D / 2; idx += blockDim.x) {
     const int g = (2 * idx) / D, d = 2 * idx - g * D;
-    float o0 = 0.f, o1 = 0.f;
     const float* po = a.part_o + (pbase * G + g) * D + d;
+    float M = -INFINITY, lsum = 0.f, o0 = 0.f, o1 = 0.f;
     for (int t0 = 0; t0 < n_valid; t0 += kU) {
-      uint64_t v[kU];
-#pragma unroll
-      for (int j = 0; j < kU; ++j) v[j] = t0 + j < n_valid ? load_dev2(po + (size_t)(t0 + j) * G * D) : 0;
+      uint64_t v[kU], w[kU];
 #pragma unroll
       for (int j = 0; j < kU; ++j) {
-        // empty partials (zero sum) have weight 0 and are never written: select them away
-        const float wt = t0 + j < n_valid ? s_w[(t0 + j) * G + g] : 0.f;
-        if (wt != 0.f) {
-          o0 += wt * __uint_as_float((uint32_t)v[j]);
-          o1 += wt * __uint_as_float((uint32_t)(v[j] >> 32));
+        const bool ok = t0 + j < n_valid;
+        v[j] = ok ? load_dev2(po + (size_t)(t0 + j) * G * D) : 0;
+        w[j] = ok ? load_dev2(ml + ((t0 + j) * G + g) * 2) : 0;
+      }
+      // A split's (max, sum) is (m, l); l == 0 marks an empty partial, whose
+      // o was never written: it is selected away, never multiplied.
+      float mg = M;
+#pragma unroll
+      for (int j = 0; j < kU; ++j)
+        if (__uint_as_float((uint32_t)(w[j] >> 32)) > 0.f) mg = fmaxf(mg, __uint_as_float((uint32_t)w[j]));
+      if (mg > M) {
+        const float alpha = fast_exp2(M - mg);  // 0 while M is -inf
+        lsum *= alpha;
+        o0 *= alpha;
+        o1 *= alpha;
+        M = mg;
+      }
+#pragma unroll
+      for (int j = 0; j < kU; ++j) {
+        const float l = __uint_as_float((uint32_t)(w[j] >> 32));
+        if (l > 0.f) {
+          const float f = fast_exp2(__uint_as_float((uint32_t)w[j]) - M);
+          lsum += f * l;
+          o0 += f * __uint_as_float((uint32_t)v[j]);
+          o1 += f * __uint_as_float((uint32_t)(v[j] >> 32));
         }
       }
     }
-    a.out[((size_t)b * a.n_q + hk * G + g) * D + d] = f32_to_bf16(o0);
-    a.out[((size_t)b * a.n_q + hk * G + g) * D + d + 1] = f32_to_bf16(o1);
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    a.out[((size_t)b * a.n_q + hk * G + g) * D + d] = f32_to_bf16(o0 * inv);
+    a.out[((size_t)b * a.n_q + hk * G + g) * D + d + 1] = f32_to_bf16(o1 * inv);
+    if (a.lse && d == 0)
+      a.lse[(size_t)b * a.n_q + hk * G + g] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
   }
 }
 
 // Writes this workgroup's result: the final output when it is the row's only
 // split, else its unnormalised partial (o, running max in log2 units, sum),
 // and the last split to arrive merges all partials.  o_val(g, d), Mof(g),
-// Lof(g) give the workgroup's values; s_w is LDS free for the merge weights
-// (>= n_valid * G floats, not read by o_val / Mof / Lof).
+// Lof(g) give the workgroup's values.
 template <int D, class OFn, class MFn, class LFn>
 __device__ void finish(const DecodeArgs& a, const RowRange& r, int b, int hk, int s, OFn o_val,
-                       MFn Mof, LFn Lof, float* s_w) {
+                       MFn Mof, LFn Lof) {
   const int G = a.G;
   const int tid = threadIdx.x;
   if (r.n_valid <= 1) {
@@ -224,7 +225,7 @@ __device__ void finish(const DecodeArgs& a, const RowRange& r, int b, int hk, in
     s_last = old == (uint32_t)(r.n_valid - 1);
   }
   __syncthreads();
-  if (s_last) merge_splits<D>(a, b, hk, r.n_valid, s_w);
+  if (s_last) merge_splits<D>(a, b, hk, r.n_valid);
 }
 
 // An idle row (padding slot or empty context): split 0 writes out = 0 and
@@ -244,7 +245,6 @@ template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_keysplit_kernel(DecodeArgs a) {
   extern __shared__ float s_o[];                  // [wave][G][D] (dynamic: NW * G * D)
-  __shared__ float s_w[kMaxMergeWeights];         // merge weights (last split of a row)
   __shared__ int s_pg[kSegPages];
   __shared__ float s_ml[2 * NW * 16];             // [wave][16] max, then sum
   __shared__ float s_red[NW * 16 + 32];
@@ -410,7 +410,7 @@ void decode_keysplit_kernel(DecodeArgs a) {
   };
   auto Mof = [&](int g) { return s_red[NW * 16 + g]; };
   auto Lof = [&](int g) { return s_red[NW * 16 + 16 + g]; };
-  finish<D>(a, r, b, hk, s, o_val, Mof, Lof, s_w);
+  finish<D>(a, r, b, hk, s, o_val, Mof, Lof);
 }
 
 // ---------------------------------------------------------------------------
@@ -421,7 +421,6 @@ __global__ __launch_bounds__(kThreads) void decode_dimsplit_kernel(DecodeArgs a)
   __shared__ int s_pg[kSegPages];
   __shared__ f32x4 s_part[2][kDecodeWaves][2][64];  // [buffer][wave][rg][lane]
   __shared__ float s_o[kMaxGD];                     // [G][D] final unnormalised output
-  __shared__ float s_w[kMaxMergeWeights];           // merge weights (last split of a row)
   __shared__ float s_ml[32];
   const int s = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -553,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void decode_dimsplit_kernel(DecodeArgs a)
   auto o_val = [&](int g, int d) { return s_o[g * D + d]; };
   auto Mof = [&](int g) { return s_ml[g]; };
   auto Lof = [&](int g) { return s_ml[16 + g]; };
-  finish<D>(a, r, b, hk, s, o_val, Mof, Lof, s_w);
+  finish<D>(a, r, b, hk, s, o_val, Mof, Lof);
 }
 
 template <int D>
@@ -584,10 +583,10 @@ DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_h
   long split = 32 * kDecodeWaves;
   // About 2048 workgroups over the key ranges (8 per CU): enough to cover the
   // 256 CUs several times, few enough that the partials written and merged
-  // stay small next to the K/V bytes.  The split count is also capped so the
-  // merge weights of a (row, kv head) fit the 1024-float LDS buffer.
+  // stay small next to the K/V bytes.  The split count is also capped so that
+  // one merge reads at most 1024 (split, head) partials.
   while ((pairs * ((range + split - 1) / split) > 2048 ||
-          ((range + split - 1) / split) * G > kMaxMergeWeights) &&
+          ((range + split - 1) / split) * G > kMaxMergeUnits) &&
          split < (1 << 24))
     split *= 2;
   p.split_tokens = (int)split;
