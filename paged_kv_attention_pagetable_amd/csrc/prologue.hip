@@ -6,8 +6,8 @@
 // rotate_half partner of dims 8c..8c+7 lives in lane c ^ (D/16) of the same
 // row group, and the mean of squares is a xor-shuffle reduction over the
 // row's lanes.  All arithmetic is fp32; each output is rounded to bf16 once.
-// grid = (ceil(T / 64), n_q + n_kv); y < n_q handles q head y, otherwise kv
-// head y - n_q (k rows and the V^T staging / store, as in the append kernel).
+// grid = (n_q + 2 n_kv, ceil(T / 64)): a workgroup handles 64 tokens of one
+// q, k or v head (the v heads stage V^T in LDS, as the append kernel does).
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -16,10 +16,13 @@ namespace pkv {
 namespace {
 
 constexpr int kProTokens = 64;
+constexpr int kCuStage = 512;  // sequences whose metadata is staged in LDS (n_seqs < this)
 
+// cs / sn: cos and sin of the lane's 8 rotary angles (frequencies f0 .. f0+7,
+// f0 = 8c mod D/2) at the row's position.
 template <int D>
-__device__ __forceinline__ u32x4 norm_rope_row(u32x4 x, const bf16_t* w, const float* cos_row,
-                                               const float* sin_row, int c, float eps) {
+__device__ __forceinline__ u32x4 norm_rope_row(u32x4 x, const bf16_t* w, const float (&cs)[8],
+                                               const float (&sn)[8], int c, float eps) {
   constexpr int LPR = D / 8;  // lanes per row
   float v[8];
 #pragma unroll
@@ -44,7 +47,6 @@ __device__ __forceinline__ u32x4 norm_rope_row(u32x4 x, const bf16_t* w, const f
 #pragma unroll
   for (int j = 0; j < 8; ++j) pr[j] = shfl_xor(v[j], LPR / 2);
   const bool first_half = c < LPR / 2;
-  const int f0 = (8 * c) & (D / 2 - 1);
   u32x4 out;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -53,39 +55,119 @@ __device__ __forceinline__ u32x4 norm_rope_row(u32x4 x, const bf16_t* w, const f
     for (int k = 0; k < 2; ++k) {
       const int j = 2 * e + k;
       const float rot = first_half ? -pr[j] : pr[j];
-      o[k] = v[j] * cos_row[f0 + j] + rot * sin_row[f0 + j];
+      o[k] = v[j] * cs[j] + rot * sn[j];
     }
     out[e] = pack_bf16x2(o[0], o[1]);
   }
   return out;
 }
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// accesses, not for its outstanding global loads (__syncthreads() would also
+// drain the row loads in flight).  The signal fences keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Sequence of token t: the last n with cu[n] <= t (cu ascending, cu[0] = 0).
+__device__ __forceinline__ int seq_of(const int32_t* cu, int n_seqs, int t) {
+  int lo = 0, hi = n_seqs;  // invariant: cu[lo] <= t < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Shared memory of one prologue workgroup.
 template <int D>
-__global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
+struct ProSmem {
+  int cu[kCuStage];
+  int slot[kCuStage];
+  int sp[kCuStage];
+  int page[kProTokens];
+  int row[kProTokens];
+  int pos[kProTokens];
+  bf16_t v[kProTokens][D + 2];  // +2: odd dword stride, no bank conflicts
+};
+
+enum { kHeadQ = 0, kHeadK = 1, kHeadV = 2 };
+
+// One workgroup: 64 tokens of one head of kind KIND (q: normalise + rotate in
+// place; k: normalise + rotate + append; v: raw append).  Each kind (and the
+// staged / global metadata form) is its own code path, so the compiler's
+// waits for one path's loads never drain another's rows in flight.
+template <int D, int KIND, bool STAGED>
+__device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>& sm, int hh) {
   constexpr int LPR = D / 8;
-  constexpr int ROWS = 256 / LPR;  // rows processed per pass by the workgroup
-  __shared__ int s_page[kProTokens];
-  __shared__ int s_row[kProTokens];
-  __shared__ int s_pos[kProTokens];
-  __shared__ bf16_t s_v[kProTokens][D + 2];
-  const int t0 = blockIdx.x * kProTokens;
-  const int hh = blockIdx.y;
+  constexpr int ROWS = 256 / LPR;              // rows processed per pass by the workgroup
+  constexpr int PASSES = kProTokens / ROWS;    // passes over the 64 tokens
+  const int t0 = blockIdx.y * kProTokens;
   const int nt = min(kProTokens, a.T - t0);
   const int tid = threadIdx.x;
   const int n_kv = a.g.n_kv, ps = a.g.page_size;
+  const int c = tid % LPR;
+  const int rsub = tid / LPR;
+  const int h = KIND == kHeadQ ? hh : (KIND == kHeadK ? hh - a.n_q : hh - a.n_q - n_kv);
+  // Sequence metadata (cu_seqlens, slots, start_pos) staged in LDS: loads
+  // issued first, the row loads right after, so the set-up overlaps the rows'
+  // latency (it waits for the metadata only; the barriers are LDS-only).
+  // Loads are unconditional with clamped indices so the waits stay partial.
+  int m_cu[kCuStage / 256], m_slot[kCuStage / 256], m_sp[kCuStage / 256];
+  if (STAGED) {
+#pragma unroll
+    for (int j = 0; j < kCuStage / 256; ++j) {
+      const int i = tid + 256 * j;
+      m_cu[j] = a.cu_seqlens[min(i, a.n_seqs)];
+      m_slot[j] = a.slots[min(i, a.n_seqs - 1)];
+      m_sp[j] = a.start_pos ? a.start_pos[min(i, a.n_seqs - 1)] : 0;
+    }
+  }
+  // This thread's rows.  Rows past the last token re-read token t0 (in
+  // bounds) and are never stored.
+  const bf16_t* src = KIND == kHeadQ ? a.q : (KIND == kHeadK ? a.k_raw : a.v_raw);
+  const int src_heads = KIND == kHeadQ ? a.n_q : n_kv;
+  u32x4 x[PASSES];
+#pragma unroll
+  for (int k = 0; k < PASSES; ++k) {
+    const int tt = rsub + k * ROWS;
+    const int tr = t0 + (tt < nt ? tt : 0);
+    x[k] = load16(src + ((size_t)tr * src_heads + h) * D + 8 * c);
+  }
+  if (STAGED) {
+#pragma unroll
+    for (int j = 0; j < kCuStage / 256; ++j) {
+      const int i = tid + 256 * j;
+      if (i <= a.n_seqs) sm.cu[i] = m_cu[j];
+      if (i < a.n_seqs) {
+        sm.slot[i] = m_slot[j];
+        sm.sp[i] = m_sp[j];
+      }
+    }
+    lds_barrier();
+  }
   if (tid < nt) {
     const int t = t0 + tid;
-    // sequence of token t: last n with cu_seqlens[n] <= t
-    int lo = 0, hi = a.n_seqs;  // invariant: cu[lo] <= t < cu[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.cu_seqlens[mid] <= t) lo = mid; else hi = mid;
+    int n, cu_n, slot, sp;
+    if (STAGED) {
+      n = seq_of(sm.cu, a.n_seqs, t);
+      cu_n = sm.cu[n];
+      slot = sm.slot[n];
+      sp = sm.sp[n];
+    } else {
+      n = seq_of(a.cu_seqlens, a.n_seqs, t);
+      cu_n = a.cu_seqlens[n];
+      slot = a.slots[n];
+      sp = a.start_pos ? a.start_pos[n] : 0;
     }
-    const int slot = a.slots[lo];
-    const int pos = (a.start_pos ? a.start_pos[lo] : 0) + (t - a.cu_seqlens[lo]);
+    const int pos = sp + (t - cu_n);
     int page = -1, row = 0;
-    bool ok = slot > 0 && slot < a.pt.max_slots && pos >= 0 && pos < a.max_pos;
-    if (ok) {
+    const bool ok = slot > 0 && slot < a.pt.max_slots && pos >= 0 && pos < a.max_pos;
+    if (KIND != kHeadQ && ok) {  // q rows need only the position
       const int lp = pos >> a.g.log2ps;
       if (lp < a.pt.pps) {
         const int pg = a.pt.table[(size_t)slot * a.pt.pps + lp];
@@ -95,58 +177,96 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
         }
       }
     }
-    s_page[tid] = page;
-    s_row[tid] = row;
-    s_pos[tid] = ok ? pos : -1;
+    sm.page[tid] = page;
+    sm.row[tid] = row;
+    sm.pos[tid] = ok ? pos : -1;
   }
-  __syncthreads();
-  const int c = tid % LPR;
-  const int rsub = tid / LPR;
+  lds_barrier();
   const size_t blk = (size_t)ps * D;
   const size_t page_stride = (size_t)n_kv * blk;
-  if (hh < a.n_q) {
-    for (int tt = rsub; tt < nt; tt += ROWS) {
-      const int pos = s_pos[tt];
-      if (pos < 0) continue;  // uniform over the row's lanes
-      bf16_t* row = a.q + ((size_t)(t0 + tt) * a.n_q + hh) * D;
-      const u32x4 x = load16(row + 8 * c);
-      const u32x4 y = norm_rope_row<D>(x, a.q_w, a.cos_t + (size_t)pos * (D / 2),
-                                       a.sin_t + (size_t)pos * (D / 2), c, a.eps);
-      store16(row + 8 * c, y);
+  if (KIND == kHeadV) {
+    // raw V rows -> LDS staging, then stored transposed: lanes on
+    // consecutive tokens, so tokens sharing a page and key group are
+    // contiguous
+#pragma unroll
+    for (int k = 0; k < PASSES; ++k) {
+      const int tt = rsub + k * ROWS;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sm.v[tt][8 * c + 2 * e] = (bf16_t)(x[k][e] & 0xffffu);
+        sm.v[tt][8 * c + 2 * e + 1] = (bf16_t)(x[k][e] >> 16);
+      }
+    }
+    lds_barrier();
+    for (int i = tid; i < D * kProTokens; i += 256) {
+      const int d = i / kProTokens, tt = i - d * kProTokens;
+      if (tt >= nt) continue;
+      const int page = sm.page[tt];
+      if (page < 0 || sm.pos[tt] < 0) continue;
+      a.vpool[(size_t)page * page_stride + h * blk + v_elem_offset(d, sm.row[tt], D, a.g.log2ps)] = sm.v[tt][d];
     }
     return;
   }
-  const int h = hh - a.n_q;
-  for (int tt = rsub; tt < nt; tt += ROWS) {
-    const int pos = s_pos[tt];
-    const int page = s_page[tt];
-    const size_t src = ((size_t)(t0 + tt) * n_kv + h) * D + 8 * c;
-    if (pos >= 0 && page >= 0) {
-      const u32x4 x = load16(a.k_raw + src);
-      const u32x4 y = norm_rope_row<D>(x, a.k_w, a.cos_t + (size_t)pos * (D / 2),
-                                       a.sin_t + (size_t)pos * (D / 2), c, a.eps);
-      store16(a.kpool + (size_t)page * page_stride + h * blk + (size_t)s_row[tt] * D + 8 * c, y);
-    }
-    const u32x4 vv = load16(a.v_raw + src);
+  int pos_k[PASSES];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s_v[tt][8 * c + 2 * e] = (bf16_t)(vv[e] & 0xffffu);
-      s_v[tt][8 * c + 2 * e + 1] = (bf16_t)(vv[e] >> 16);
+  for (int k = 0; k < PASSES; ++k) {
+    const int tt = rsub + k * ROWS;
+    pos_k[k] = tt < nt ? sm.pos[tt] : -1;
+  }
+  const int f0 = (8 * c) & (D / 2 - 1);
+  float cs[PASSES][8], sn[PASSES][8];
+#pragma unroll
+  for (int k = 0; k < PASSES; ++k) {
+    const size_t ro = (size_t)max(pos_k[k], 0) * (D / 2) + f0;
+#pragma unroll
+    for (int j = 0; j < 8; j += 4) {
+      const f32x4 cv = *reinterpret_cast<const f32x4*>(a.cos_t + ro + j);
+      const f32x4 sv = *reinterpret_cast<const f32x4*>(a.sin_t + ro + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cs[k][j + e] = cv[e];
+        sn[k][j + e] = sv[e];
+      }
     }
   }
-  __syncthreads();
-  for (int i = tid; i < D * kProTokens; i += 256) {
-    const int d = i / kProTokens, tt = i - d * kProTokens;
-    if (tt >= nt) continue;
-    const int page = s_page[tt];
-    if (page < 0 || s_pos[tt] < 0) continue;
-    a.vpool[(size_t)page * page_stride + h * blk + v_elem_offset(d, s_row[tt], D, a.g.log2ps)] = s_v[tt][d];
+  const bf16_t* w = KIND == kHeadQ ? a.q_w : a.k_w;
+#pragma unroll
+  for (int k = 0; k < PASSES; ++k) {
+    const int tt = rsub + k * ROWS;
+    if (pos_k[k] < 0) continue;  // uniform over the row's lanes
+    const u32x4 y = norm_rope_row<D>(x[k], w, cs[k], sn[k], c, a.eps);
+    if (KIND == kHeadQ) {
+      store16(a.q + ((size_t)(t0 + tt) * a.n_q + h) * D + 8 * c, y);
+    } else if (sm.page[tt] >= 0) {
+      store16(a.kpool + (size_t)sm.page[tt] * page_stride + h * blk + (size_t)sm.row[tt] * D + 8 * c, y);
+    }
+  }
+}
+
+// grid = (n_q + 2 n_kv, ceil(T / 64)): x < n_q is q head x, then the k
+// heads, then the v heads.
+template <int D>
+__global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
+  __shared__ ProSmem<D> sm;
+  const int hh = blockIdx.x;
+  const int kind = hh < a.n_q ? kHeadQ : (hh < a.n_q + a.g.n_kv ? kHeadK : kHeadV);
+  if (a.n_seqs < kCuStage) {
+    if (kind == kHeadQ) prologue_body<D, kHeadQ, true>(a, sm, hh);
+    else if (kind == kHeadK) prologue_body<D, kHeadK, true>(a, sm, hh);
+    else prologue_body<D, kHeadV, true>(a, sm, hh);
+  } else {
+    if (kind == kHeadQ) prologue_body<D, kHeadQ, false>(a, sm, hh);
+    else if (kind == kHeadK) prologue_body<D, kHeadK, false>(a, sm, hh);
+    else prologue_body<D, kHeadV, false>(a, sm, hh);
   }
 }
 
 template <int D>
 hipError_t launch_prologue_d(const PrologueArgs& a, hipStream_t st) {
-  dim3 grid((a.T + kProTokens - 1) / kProTokens, a.n_q + a.g.n_kv);
+  // Heads vary fastest: the workgroups in flight cover all heads of a few
+  // token blocks, i.e. contiguous [token][head][D] memory, not one head's
+  // 256-byte pieces strided across many tokens.
+  dim3 grid(a.n_q + 2 * a.g.n_kv, (a.T + kProTokens - 1) / kProTokens);
   hipLaunchKernelGGL((prologue_kernel<D>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -145,12 +145,8 @@ def _oracle_with_prologue(case, okp, ovp):
     return q2, q2b, k2
 
 
-@pytest.mark.parametrize("name", ["tiny", "d128_g4_ragged", "d128_g4_prefix", "d256_w64",
-                                  "slot0_pad"])
-def test_prefill_with_prologue_matches_oracle(name):
-    case = _case(name, seed=7)
-    kp, vp, table, okp, ovp = _pools_with_prefix(case)
-    q, out = _run_with_prologue(case, kp, vp, table)
+def _check_with_prologue(case, kp, vp, table, okp, ovp, name, hint=None):
+    q, out = _run_with_prologue(case, kp, vp, table, hint=hint)
     q2, q2b, k2 = _oracle_with_prologue(case, okp, ovp)
     tsl = case.token_slots()
     live = tsl != 0
@@ -170,6 +166,37 @@ def test_prefill_with_prologue_matches_oracle(name):
     ref, _ = oracle.attn_prefill(q2b, okp, ovp, case.table, case.cu_seqlens, case.slots,
                                  case.start_pos, case.scale, case.window)
     assert_attn_close(host_f64(out), ref, name)
+
+
+@pytest.mark.parametrize("name", ["tiny", "d128_g4_ragged", "d128_g4_prefix", "d256_w64",
+                                  "slot0_pad"])
+def test_prefill_with_prologue_matches_oracle(name):
+    case = _case(name, seed=7)
+    kp, vp, table, okp, ovp = _pools_with_prefix(case)
+    _check_with_prologue(case, kp, vp, table, okp, ovp, name)
+
+
+def test_prefill_with_prologue_many_sequences():
+    """601 prompts with cached prefixes: the prologue's sequence metadata is
+    too long to stage and is searched in global memory."""
+    rng = np.random.default_rng(31)
+    lengths = [int(x) for x in rng.integers(1, 12, size=600)] + [70]
+    sp = [int(x) for x in rng.integers(0, 20, size=601)]
+    case = make_prefill_case(8, 2, 64, 16, lengths, seed=2300, start_pos=sp,
+                             max_slots=len(lengths) + 1)
+    kp, vp, table, okp, ovp = _pools_with_prefix(case)
+    _check_with_prologue(case, kp, vp, table, okp, ovp, "601 prompts", hint=8)
+
+
+def test_prefill_with_prologue_staged_metadata_boundary():
+    """511 prompts (the largest count whose metadata the prologue stages)."""
+    rng = np.random.default_rng(32)
+    lengths = [int(x) for x in rng.integers(1, 9, size=511)]
+    sp = [int(x) for x in rng.integers(0, 9, size=511)]
+    case = make_prefill_case(8, 2, 64, 16, lengths, seed=2400, start_pos=sp,
+                             max_slots=len(lengths) + 1)
+    kp, vp, table, okp, ovp = _pools_with_prefix(case)
+    _check_with_prologue(case, kp, vp, table, okp, ovp, "511 prompts")
 
 
 def test_rope_table_matches_fp64():
