@@ -6,8 +6,9 @@
 // rotate_half partner of dims 8c..8c+7 lives in lane c ^ (D/16) of the same
 // row group, and the mean of squares is a xor-shuffle reduction over the
 // row's lanes.  All arithmetic is fp32; each output is rounded to bf16 once.
-// grid = (n_q + 2 n_kv, ceil(T / 64)): a workgroup handles 64 tokens of one
-// q, k or v head (the v heads stage V^T in LDS, as the append kernel does).
+// grid = (ceil(n_q/4) + ceil(n_kv/4) + n_kv, ceil(T / 64)): a workgroup
+// handles 64 tokens of up to 4 q heads, of up to 4 k heads, or of one v head
+// (the v heads stage V^T in LDS, as the append kernel does).
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -16,6 +17,9 @@ namespace pkv {
 namespace {
 
 constexpr int kProTokens = 64;
+// q or k heads per workgroup (fewer at head_dim 256, for registers)
+template <int D>
+constexpr int pro_heads() { return D >= 256 ? 2 : 4; }
 constexpr int kCuStage = 512;  // sequences whose metadata is staged in LDS (n_seqs < this)
 
 // cs / sn: cos and sin of the lane's 8 rotary angles (frequencies f0 .. f0+7,
@@ -102,7 +106,9 @@ enum { kHeadQ = 0, kHeadK = 1, kHeadV = 2 };
 // staged / global metadata form) is its own code path, so the compiler's
 // waits for one path's loads never drain another's rows in flight.
 template <int D, int KIND, bool STAGED>
-__device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>& sm, int hh) {
+__device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>& sm, int h0) {
+  // q / k workgroups take pro_heads<D>() heads of the same tokens (the cos /
+  // sin of a token serve all of them); v workgroups one head.
   constexpr int LPR = D / 8;
   constexpr int ROWS = 256 / LPR;              // rows processed per pass by the workgroup
   constexpr int PASSES = kProTokens / ROWS;    // passes over the 64 tokens
@@ -112,7 +118,9 @@ __device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>&
   const int n_kv = a.g.n_kv, ps = a.g.page_size;
   const int c = tid % LPR;
   const int rsub = tid / LPR;
-  const int h = KIND == kHeadQ ? hh : (KIND == kHeadK ? hh - a.n_q : hh - a.n_q - n_kv);
+  constexpr int HN = KIND == kHeadV ? 1 : pro_heads<D>();
+  const int n_heads = KIND == kHeadQ ? a.n_q : n_kv;  // heads of this kind
+  const int h = h0;  // first head of the workgroup
   // Sequence metadata (cu_seqlens, slots, start_pos) staged in LDS: loads
   // issued first, the row loads right after, so the set-up overlaps the rows'
   // latency (it waits for the metadata only; the barriers are LDS-only).
@@ -131,12 +139,14 @@ __device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>&
   // bounds) and are never stored.
   const bf16_t* src = KIND == kHeadQ ? a.q : (KIND == kHeadK ? a.k_raw : a.v_raw);
   const int src_heads = KIND == kHeadQ ? a.n_q : n_kv;
-  u32x4 x[PASSES];
+  u32x4 x[PASSES][HN];
 #pragma unroll
   for (int k = 0; k < PASSES; ++k) {
     const int tt = rsub + k * ROWS;
     const int tr = t0 + (tt < nt ? tt : 0);
-    x[k] = load16(src + ((size_t)tr * src_heads + h) * D + 8 * c);
+#pragma unroll
+    for (int j = 0; j < HN; ++j)
+      x[k][j] = load16(src + ((size_t)tr * src_heads + min(h + j, n_heads - 1)) * D + 8 * c);
   }
   if (STAGED) {
 #pragma unroll
@@ -193,8 +203,8 @@ __device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>&
       const int tt = rsub + k * ROWS;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sm.v[tt][8 * c + 2 * e] = (bf16_t)(x[k][e] & 0xffffu);
-        sm.v[tt][8 * c + 2 * e + 1] = (bf16_t)(x[k][e] >> 16);
+        sm.v[tt][8 * c + 2 * e] = (bf16_t)(x[k][0][e] & 0xffffu);
+        sm.v[tt][8 * c + 2 * e + 1] = (bf16_t)(x[k][0][e] >> 16);
       }
     }
     lds_barrier();
@@ -234,30 +244,38 @@ __device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>&
   for (int k = 0; k < PASSES; ++k) {
     const int tt = rsub + k * ROWS;
     if (pos_k[k] < 0) continue;  // uniform over the row's lanes
-    const u32x4 y = norm_rope_row<D>(x[k], w, cs[k], sn[k], c, a.eps);
-    if (KIND == kHeadQ) {
-      store16(a.q + ((size_t)(t0 + tt) * a.n_q + h) * D + 8 * c, y);
-    } else if (sm.page[tt] >= 0) {
-      store16(a.kpool + (size_t)sm.page[tt] * page_stride + h * blk + (size_t)sm.row[tt] * D + 8 * c, y);
+#pragma unroll
+    for (int j = 0; j < HN; ++j) {
+      if (h + j >= n_heads) break;  // uniform over the workgroup
+      const u32x4 y = norm_rope_row<D>(x[k][j], w, cs[k], sn[k], c, a.eps);
+      if (KIND == kHeadQ) {
+        store16(a.q + ((size_t)(t0 + tt) * a.n_q + h + j) * D + 8 * c, y);
+      } else if (sm.page[tt] >= 0) {
+        store16(a.kpool + (size_t)sm.page[tt] * page_stride + (h + j) * blk + (size_t)sm.row[tt] * D + 8 * c, y);
+      }
     }
   }
 }
 
-// grid = (n_q + 2 n_kv, ceil(T / 64)): x < n_q is q head x, then the k
-// heads, then the v heads.
+// grid = (nq_wg + nk_wg + n_kv, ceil(T / 64)): x < nq_wg takes q heads
+// pro_heads<D>()*x .., then the k-head workgroups, then one per v head.
 template <int D>
 __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
   __shared__ ProSmem<D> sm;
-  const int hh = blockIdx.x;
-  const int kind = hh < a.n_q ? kHeadQ : (hh < a.n_q + a.g.n_kv ? kHeadK : kHeadV);
+  const int nq_wg = (a.n_q + pro_heads<D>() - 1) / pro_heads<D>();
+  const int nk_wg = (a.g.n_kv + pro_heads<D>() - 1) / pro_heads<D>();
+  const int x = blockIdx.x;
+  const int kind = x < nq_wg ? kHeadQ : (x < nq_wg + nk_wg ? kHeadK : kHeadV);
+  const int h0 = kind == kHeadQ ? pro_heads<D>() * x
+               : (kind == kHeadK ? pro_heads<D>() * (x - nq_wg) : x - nq_wg - nk_wg);
   if (a.n_seqs < kCuStage) {
-    if (kind == kHeadQ) prologue_body<D, kHeadQ, true>(a, sm, hh);
-    else if (kind == kHeadK) prologue_body<D, kHeadK, true>(a, sm, hh);
-    else prologue_body<D, kHeadV, true>(a, sm, hh);
+    if (kind == kHeadQ) prologue_body<D, kHeadQ, true>(a, sm, h0);
+    else if (kind == kHeadK) prologue_body<D, kHeadK, true>(a, sm, h0);
+    else prologue_body<D, kHeadV, true>(a, sm, h0);
   } else {
-    if (kind == kHeadQ) prologue_body<D, kHeadQ, false>(a, sm, hh);
-    else if (kind == kHeadK) prologue_body<D, kHeadK, false>(a, sm, hh);
-    else prologue_body<D, kHeadV, false>(a, sm, hh);
+    if (kind == kHeadQ) prologue_body<D, kHeadQ, false>(a, sm, h0);
+    else if (kind == kHeadK) prologue_body<D, kHeadK, false>(a, sm, h0);
+    else prologue_body<D, kHeadV, false>(a, sm, h0);
   }
 }
 
@@ -266,7 +284,9 @@ hipError_t launch_prologue_d(const PrologueArgs& a, hipStream_t st) {
   // Heads vary fastest: the workgroups in flight cover all heads of a few
   // token blocks, i.e. contiguous [token][head][D] memory, not one head's
   // 256-byte pieces strided across many tokens.
-  dim3 grid(a.n_q + 2 * a.g.n_kv, (a.T + kProTokens - 1) / kProTokens);
+  const int nq_wg = (a.n_q + pro_heads<D>() - 1) / pro_heads<D>();
+  const int nk_wg = (a.g.n_kv + pro_heads<D>() - 1) / pro_heads<D>();
+  dim3 grid(nq_wg + nk_wg + a.g.n_kv, (a.T + kProTokens - 1) / kProTokens);
   hipLaunchKernelGGL((prologue_kernel<D>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
