@@ -313,9 +313,19 @@ def _pmc_per_kernel(db_path, counter):
     return acc
 
 
-def summarize_pmc(fetch_db, write_db, out_prefix, workload="qwen3_decode", command=""):
-    """HBM bytes per decode call = (split + merge) FETCH_SIZE + WRITE_SIZE (KiB per
-    dispatch), each scaled by what the counter reads for a 256 MiB device copy."""
+PMC_PARTS = {
+    # part: (kernel-name key counted per call, sources whose hash the record keeps)
+    "decode": ("decode_", ["decode.hip", "pkv_device.h", "pkv_internal.h"]),
+    "prefill": ("prefill_kernel", ["prefill.hip", "pkv_device.h", "pkv_internal.h"]),
+}
+
+
+def summarize_pmc(fetch_db, write_db, out_prefix, workload="qwen3_decode", command="",
+                  part="decode"):
+    """HBM bytes per call of the part's attention kernel = FETCH_SIZE + WRITE_SIZE
+    (KiB per dispatch), each scaled by what the counter reads for a 256 MiB device
+    copy.  Other library kernels of the run are listed for reference."""
+    key, sources = PMC_PARTS[part]
     fetch = _pmc_per_kernel(fetch_db, "FETCH_SIZE")
     write = _pmc_per_kernel(write_db, "WRITE_SIZE")
     copy_bytes = 128 * 2**20 * 2
@@ -328,16 +338,16 @@ def summarize_pmc(fetch_db, write_db, out_prefix, workload="qwen3_decode", comma
     per_call = 0.0
     parts = {}
     for k in sorted(set(fetch) | set(write)):
-        if "pkv::" not in k or "decode_" not in k:
+        if "pkv::" not in k:
             continue
         fb = float(np.mean(fetch.get(k, [0.0]))) * 1024.0 * (f_scale or 1.0)
         wb = float(np.mean(write.get(k, [0.0]))) * 1024.0 * (w_scale or 1.0)
-        per_call += fb + wb
+        if key in k:
+            per_call += fb + wb
         short = k.replace("void ", "").replace("pkv::(anonymous namespace)::", "").split("(")[0]
         parts[short] = dict(fetch_bytes=round(fb), write_bytes=round(wb),
-                            dispatches=len(fetch.get(k, [])))
-    sources = ["decode.hip", "pkv_device.h", "pkv_internal.h"]
-    rec = dict(workload=workload, source_sha=source_sha(sources),
+                            dispatches=len(fetch.get(k, [])), counted=key in k)
+    rec = dict(workload=workload, part=part, source_sha=source_sha(sources),
                hbm_bytes_per_call=round(per_call), kernels=parts,
                copy_scale=dict(fetch=f_scale, write=w_scale, copy_bytes=copy_bytes),
                command=command)
@@ -454,15 +464,18 @@ def main():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DB", "OUT"),
                     help="write a kernel-duration summary of a rocprofv3 database and exit")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "OUT"),
-                    help="write HBM traffic per decode call from two rocprofv3 --pmc runs "
-                         "(FETCH_SIZE, WRITE_SIZE) and exit")
+                    help="write HBM traffic per attention call from two rocprofv3 --pmc "
+                         "runs (FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--pmc-part", default="decode", choices=sorted(PMC_PARTS),
+                    help="which attention kernel --summarize-pmc counts per call")
     ap.add_argument("--command", default="", help="command line recorded in summaries")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, command=args.command)
         return
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc, workload=args.workload, command=args.command)
+        summarize_pmc(*args.summarize_pmc, workload=args.workload, command=args.command,
+                      part=args.pmc_part)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this bench runs the single-GPU path only; "
@@ -489,8 +502,7 @@ def main():
     step_bytes = sum(attn_bytes) + sum(wl.append_bytes(ly) for ly in wl.layers)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = (sum(attn_bytes) / wl.n_calls) / (ms_attn * 1e-3) / 1e9
-    dec_sources = ["decode.hip", "pkv_device.h", "pkv_internal.h"]
-    traffic = pmc_traffic(f"decode_{args.workload}", dec_sources)
+    traffic = pmc_traffic(f"decode_{args.workload}", PMC_PARTS["decode"][1])
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                     kernel="decode attention (split-K kernel, last split merges)",
@@ -528,7 +540,8 @@ def main():
             "roofline": dict(bound="mfma", achieved=round(tflops, 2),
                              peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                              frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                             traffic=None, kernel="prefill attention",
+                             traffic=pmc_traffic("prefill_qwen3_prefill", PMC_PARTS["prefill"][1]),
+                             kernel="prefill attention",
                              algorithmic_flops_per_call=fl, us_per_call=round(ms_pa * 1e3, 3)),
             "prologue_bytes_per_call": pw.prologue_bytes(),
         }
