@@ -210,8 +210,10 @@ class PrefillWorkload:
         return int((2 * 2 * c["head_dim"] * c["n_q"] * L * (L + 1) // 2).sum())
 
     def prologue_bytes(self):
+        """Bytes of the prologue kernel: k and v rows read and written (q's norm
+        and rotation run inside the attention kernel, which reads q anyway)."""
         c, T = self.c, self.case.T
-        rows = T * (c["n_q"] + 2 * c["n_kv"])
+        rows = T * 2 * c["n_kv"]
         return rows * c["head_dim"] * 2 * 2   # read + write
 
     def describe(self):

@@ -89,13 +89,14 @@ typedef struct {
 /* Fused Qwen3 prologue for prefill: per token and head,
  *   x <- RMSNorm(x) * w  over head_dim  (fp32: x / sqrt(mean(x^2) + eps) * w)
  *   x <- x * cos + rotate_half(x) * sin, rotate_half(x) = (-x[D/2:], x[:D/2])
- * applied to q (in place) and k; the new k and the raw v are appended to the
- * pages.  Order and formulas: [moe-qwen3 compare]
+ * applied to k, which is then appended to the pages with the raw v, and to q
+ * inside the attention kernel as it loads q (q in memory is not modified).  Order and formulas: [moe-qwen3 compare]
  * unsloth/inference/flex_gemma4_moe.py, attention forward (q_norm / k_norm,
  * then rotary, then the paged-KV write) and _rotate_half / _apply_rotary_full.
  * The cos/sin tables are fp32 [max_pos][head_dim/2] (see pkv_rope_table); a
- * token at position p uses row p.  Positions >= max_pos are an error on the
- * device side: the token is skipped (not appended, q left raw). */
+ * token at position p uses row p.  Positions >= max_pos are a caller error:
+ * such a token's k is not appended and its q reads row max_pos-1 (in bounds;
+ * its results are unspecified). */
 typedef struct {
   const void* q_norm_w;   /* device bf16 [head_dim]                     */
   const void* k_norm_w;   /* device bf16 [head_dim]                     */
@@ -180,10 +181,12 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t n_q_heads, int32_t n_kv_head
  * flex_gemma4_moe.py, _create_prefill_sliding_blockmask).  Packing follows the
  * engine's _prefill (prompts concatenated, positions restart at 0 per prompt).
  * With `pro` == NULL every key must already be in the pages (e.g. through
- * pkv_append); with `pro` != NULL the prologue first normalises and rotates q
- * in place and k, and appends k and the raw v at the queries' positions.
- *   q          : device bf16 [total_tokens][n_q_heads][head_dim]
- *                (rewritten in place when pro != NULL)
+ * pkv_append); with `pro` != NULL a prologue kernel first normalises and
+ * rotates k and appends k and the raw v at the queries' positions, and the
+ * attention kernel normalises and rotates q in registers as it loads it.
+ *   q          : device bf16 [total_tokens][n_q_heads][head_dim], raw (before
+ *                the prologue's norm and rotation when pro != NULL); not
+ *                modified
  *   cu_seqlens : device int32 [n_seqs+1], non-decreasing, cu[0] = 0,
  *                cu[n_seqs] = total_tokens
  *   slots      : device int32 [n_seqs]; slot 0 = padding sequence: its rows
@@ -198,7 +201,7 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t n_q_heads, int32_t n_kv_head
  * head_dim 512, pages_per_slot > 2048, n_seqs > 65535 and, with the
  * prologue, total_tokens > 4194240 are not supported here (PKV_ERR_UNSUPPORTED).
  */
-pkv_status pkv_attn_prefill(void* q, int32_t n_q_heads, const int32_t* cu_seqlens,
+pkv_status pkv_attn_prefill(const void* q, int32_t n_q_heads, const int32_t* cu_seqlens,
                             const int32_t* slots, const int32_t* start_pos,
                             int32_t n_seqs, int32_t total_tokens,
                             int32_t max_seqlen_q_hint, pkv_page_table pt,

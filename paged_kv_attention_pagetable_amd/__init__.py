@@ -169,8 +169,9 @@ def attn_prefill(q, cu_seqlens, slots, table, k_pool, v_pool, scale=None, window
     """Packed varlen prefill attention; returns ``out [T, n_q, D]`` (bf16).
 
     ``prologue`` (optional) is a dict with ``q_norm_w, k_norm_w, eps, cos, sin,
-    k, v``: q is then normalised and rotated in place and k (normalised and
-    rotated) and v are appended before the attention.
+    k, v``: k (normalised and rotated) and v are appended before the
+    attention, and q is normalised and rotated inside the attention kernel
+    (``q`` itself is not modified).
     """
     cd, pt = _cache(k_pool, v_pool, table)
     _bits16(q, "q")

@@ -185,7 +185,7 @@ pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slot
   return launched(pkv::launch_decode(a, static_cast<hipStream_t>(stream)), fn);
 }
 
-pkv_status pkv_attn_prefill(void* q, int32_t n_q_heads, const int32_t* cu_seqlens,
+pkv_status pkv_attn_prefill(const void* q, int32_t n_q_heads, const int32_t* cu_seqlens,
                             const int32_t* slots, const int32_t* start_pos,
                             int32_t n_seqs, int32_t total_tokens,
                             int32_t max_seqlen_q_hint, pkv_page_table pt,
@@ -228,16 +228,13 @@ pkv_status pkv_attn_prefill(void* q, int32_t n_q_heads, const int32_t* cu_seqlen
     if (!(pro->eps >= 0.f) || !std::isfinite(pro->eps))
       return fail(PKV_ERR_INVALID_ARG, "%s: prologue eps must be finite and >= 0", fn);
     pkv::PrologueArgs p;
-    p.q = static_cast<pkv::bf16_t*>(q);
     p.k_raw = static_cast<const pkv::bf16_t*>(pro->k_raw);
     p.v_raw = static_cast<const pkv::bf16_t*>(pro->v_raw);
-    p.q_w = static_cast<const pkv::bf16_t*>(pro->q_norm_w);
     p.k_w = static_cast<const pkv::bf16_t*>(pro->k_norm_w);
     p.eps = pro->eps;
     p.cos_t = pro->rope_cos;
     p.sin_t = pro->rope_sin;
     p.max_pos = pro->max_pos;
-    p.n_q = n_q_heads;
     p.T = total_tokens;
     p.cu_seqlens = cu_seqlens;
     p.slots = slots;
@@ -269,6 +266,12 @@ pkv_status pkv_attn_prefill(void* q, int32_t n_q_heads, const int32_t* cu_seqlen
   if (a.n_qblocks > 65535) a.n_qblocks = 65535;
   a.out = static_cast<pkv::bf16_t*>(out);
   a.lse = lse;
+  // q's RMSNorm + RoPE run inside the attention kernel as it loads q
+  a.q_w = pro ? static_cast<const pkv::bf16_t*>(pro->q_norm_w) : nullptr;
+  a.cos_t = pro ? pro->rope_cos : nullptr;
+  a.sin_t = pro ? pro->rope_sin : nullptr;
+  a.eps = pro ? pro->eps : 0.f;
+  a.max_pos = pro ? pro->max_pos : 0;
   return launched(pkv::launch_prefill(a, s), fn);
 }
 

@@ -78,17 +78,16 @@ struct DecodeArgs {
   float* lse;            // [B][n_q] or null
 };
 
+// The prologue kernel handles k (normalise, rotate, append) and v (append);
+// q's normalisation and rotation run inside the prefill attention kernel.
 struct PrologueArgs {
-  bf16_t* q;  // [T][n_q][D], rewritten in place
   const bf16_t* k_raw;
   const bf16_t* v_raw;
-  const bf16_t* q_w;
   const bf16_t* k_w;
   float eps;
   const float* cos_t;
   const float* sin_t;
   int max_pos;
-  int n_q;
   int T;
   const int32_t* cu_seqlens;
   const int32_t* slots;
@@ -118,6 +117,13 @@ struct PrefillArgs {
   int n_qblocks;  // grid extent over query blocks (grid-stride beyond it)
   bf16_t* out;
   float* lse;
+  // Fused q RMSNorm * q_w + RoPE (q_w != null): q is read raw and transformed
+  // in registers; cos / sin rows [max_pos][D/2] fp32.
+  const bf16_t* q_w;
+  const float* cos_t;
+  const float* sin_t;
+  float eps;
+  int max_pos;
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);

@@ -206,6 +206,115 @@ struct WaveQ {
   int lo, hi;           // positions of the wave's first / last query (hi < 0: none)
 };
 
+// Sum over the four lanes l, l^16, l^32, l^48 (the 4 dim groups of a column);
+// each swap hands every lane its partner's value in one of the two outputs.
+__device__ __forceinline__ float quad_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+  const uint32_t x = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+}
+
+// Fused Qwen3 q prologue on the loaded Q^T operand: per column (token, head)
+// x <- x / sqrt(mean(x^2) + eps) * w over head_dim, then the half-split
+// rotation x_i <- x_i cos - x_{i+D/2} sin, x_{i+D/2} <- x_{i+D/2} cos + x_i sin
+// at the token's position ([moe-qwen3 compare] flex_gemma4_moe.py, attention
+// forward: q_norm, then _apply_rotary_full / _rotate_half).  A lane holds
+// dims 8*quad + 32c + j of its column: the mean of squares is a sum over the
+// column's 4 lanes, and the partner of chunk c (< D/64) is the same lane's
+// chunk c + D/64.  fp32 math, one bf16 rounding (as the operand is used).
+// Inputs of the fused q prologue, loaded right after q so that both
+// latencies overlap.
+template <int D, int NT>
+struct QRope {
+  float cs[NT][D / 64][8], sn[NT][D / 64][8];  // cos / sin of the lane's first-half dims
+  u32x4 w[D / 32];                            // q_norm weights of the lane's dims
+};
+
+template <int D, int NT>
+__device__ __forceinline__ void load_rope(const PrefillArgs& a, int quad, const WaveQ<D, NT>& wq,
+                                          QRope<D, NT>& qr) {
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) qr.w[c] = load16(a.q_w + 8 * quad + 32 * c);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    // positions past the table (caller error) read its last row: in bounds
+    const int pos = min(max(wq.pcol[nt], 0), a.max_pos - 1);
+    const float* crow = a.cos_t + (size_t)pos * (D / 2) + 8 * quad;
+    const float* srow = a.sin_t + (size_t)pos * (D / 2) + 8 * quad;
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; j += 4) {
+        const f32x4 cv = *reinterpret_cast<const f32x4*>(crow + 32 * c + j);
+        const f32x4 sv = *reinterpret_cast<const f32x4*>(srow + 32 * c + j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qr.cs[nt][c][j + e] = cv[e];
+          qr.sn[nt][c][j + e] = sv[e];
+        }
+      }
+  }
+}
+
+// PRE: the rotary inputs were loaded by load_rope into *qr; otherwise they
+// are loaded here, 16 bytes at a time as they are used.
+template <int D, int NT, bool PRE>
+__device__ __forceinline__ void norm_rope_q(const PrefillArgs& a, int quad,
+                                            const QRope<PRE ? D : 64, NT>* qr, WaveQ<D, NT>& wq) {
+  constexpr int C = D / 32;   // 16-byte chunks per lane
+  constexpr int H = D / 64;   // chunks in the first half of the dims
+  auto wgt = [&](int c) { return PRE ? qr->w[c] : load16(a.q_w + 8 * quad + 32 * c); };
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int pos = min(max(wq.pcol[nt], 0), a.max_pos - 1);
+    const float* crow = a.cos_t + (size_t)pos * (D / 2) + 8 * quad;
+    const float* srow = a.sin_t + (size_t)pos * (D / 2) + 8 * quad;
+    auto csv = [&](int c, int j) {
+      return PRE ? qr->cs[nt][c][j] : crow[32 * c + j];
+    };
+    auto snv = [&](int c, int j) {
+      return PRE ? qr->sn[nt][c][j] : srow[32 * c + j];
+    };
+    float x[C][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[c][2 * e] = bf16lo(wq.q[nt][c][e]);
+        x[c][2 * e + 1] = bf16hi(wq.q[nt][c][e]);
+        ss += x[c][2 * e] * x[c][2 * e] + x[c][2 * e + 1] * x[c][2 * e + 1];
+      }
+    ss = quad_sum(ss);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const u32x4 wv = wgt(c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[c][2 * e] = x[c][2 * e] * inv * bf16lo(wv[e]);
+        x[c][2 * e + 1] = x[c][2 * e + 1] * inv * bf16hi(wv[e]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < H; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float lo = x[c][j], hi = x[c + H][j], cs = csv(c, j), sn = snv(c, j);
+        x[c][j] = lo * cs - hi * sn;
+        x[c + H][j] = hi * cs + lo * sn;
+      }
+    if (wq.pcol[nt] < 0) continue;  // no query: the operand stays zero
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      wq.q[nt][c] = u32x4{pack_bf16x2(x[c][0], x[c][1]), pack_bf16x2(x[c][2], x[c][3]),
+                          pack_bf16x2(x[c][4], x[c][5]), pack_bf16x2(x[c][6], x[c][7])};
+  }
+}
+
 template <int D, int NT>
 __device__ __forceinline__ void load_q(const PrefillArgs& a, const Item& it, int w, int lane,
                                        WaveQ<D, NT>& wq) {
@@ -470,7 +579,8 @@ __device__ __forceinline__ void store_out(const PrefillArgs& a, const Item& it, 
 // One work item end to end: stage its page ids, stream its key chunks through
 // the two LDS tile buffers (the next chunk's copy in flight while the current
 // one is computed), normalise and store.
-template <int D, int NT>
+// RQ: q arrives raw and gets the fused Qwen3 norm + rotation (norm_rope_q).
+template <int D, int NT, bool RQ>
 __device__ __forceinline__ void run_item(const PrefillArgs& a, int hk, int n, int qb, uint8_t* lds,
                                          int* s_pg, const LaneConst<D>& lc, int tid, int lane,
                                          int w, float inv_c) {
@@ -479,6 +589,18 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, int hk, int n, in
   item_init(a, hk, n, qb, it);
   WaveQ<D, NT> wq;
   load_q<D, NT>(a, it, w, lane, wq);
+  if constexpr (RQ) {
+    // head_dim <= 128: the rotary inputs are loaded with q, into registers;
+    // head_dim 256 holds twice as many per lane and loads them per chunk
+    // inside the transform, to stay within the register budget
+    if constexpr (D <= 128) {
+      QRope<D, NT> qr;
+      load_rope<D, NT>(a, quad, wq, qr);
+      norm_rope_q<D, NT, true>(a, quad, &qr, wq);
+    } else {
+      norm_rope_q<D, NT, false>(a, quad, nullptr, wq);
+    }
+  }
   SoftmaxAcc<D, NT> sa;
   acc_init(sa);
   __syncthreads();  // the previous item's tiles and page ids are consumed
@@ -506,7 +628,7 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, int hk, int n, in
 // workgroup whose layer exceeds its sequence's block count exits at once).
 // Grid x = kv head: with n_kv a multiple of 8 the XCDs (every 8th workgroup)
 // each keep their heads' K/V in their own L2.
-template <int D, int NT>
+template <int D, int NT, bool RQ>
 __global__ __launch_bounds__(prefill_threads<D>())
 __attribute__((amdgpu_waves_per_eu(prefill_waves<D>() / 2, prefill_waves<D>() / 2)))
 void prefill_kernel(PrefillArgs a) {
@@ -521,7 +643,7 @@ void prefill_kernel(PrefillArgs a) {
   const int len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
   const int nblk = (len + a.q_tokens - 1) / a.q_tokens;
   for (int qb = a.n_qblocks - 1 - (int)blockIdx.z; qb < nblk; qb += a.n_qblocks)
-    run_item<D, NT>(a, hk, n, qb, lds, s_pg, lc, tid, lane, w, inv_c);
+    run_item<D, NT, RQ>(a, hk, n, qb, lds, s_pg, lc, tid, lane, w, inv_c);
 }
 
 // ---------------------------------------------------------------------------
@@ -535,8 +657,10 @@ template <int D>
 hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t st) {
   constexpr int NT = prefill_nt<D>();
   const int lds = 2 * tile_bytes<D>();
-  static const hipError_t attr = set_lds_limit(&prefill_kernel<D, NT>, lds);
-  if (attr != hipSuccess) return attr;
+  static const hipError_t attr0 = set_lds_limit(&prefill_kernel<D, NT, false>, lds);
+  static const hipError_t attr1 = set_lds_limit(&prefill_kernel<D, NT, true>, lds);
+  if (attr0 != hipSuccess) return attr0;
+  if (attr1 != hipSuccess) return attr1;
   // An XCD hands its workgroups to its 4 shader engines round-robin and
   // dispatches in order, stalling when the next workgroup's engine is full.
   // With an even y extent every layer would send the same sequences to the
@@ -546,7 +670,10 @@ hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t st) {
   // batches).  (A 1-D grid in exact cost order, mapped in-kernel, balanced
   // the engines too but its per-workgroup set-up cost more than it saved.)
   dim3 grid(a.g.n_kv, a.n_seqs | 1, a.n_qblocks);
-  hipLaunchKernelGGL((prefill_kernel<D, NT>), grid, dim3(prefill_threads<D>()), lds, st, a);
+  if (a.q_w)
+    hipLaunchKernelGGL((prefill_kernel<D, NT, true>), grid, dim3(prefill_threads<D>()), lds, st, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, NT, false>), grid, dim3(prefill_threads<D>()), lds, st, a);
   return hipGetLastError();
 }
 

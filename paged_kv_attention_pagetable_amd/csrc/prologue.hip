@@ -1,14 +1,15 @@
-// Fused Qwen3 prefill prologue: per token and head, RMSNorm over head_dim
-// with a gain, then half-split rotary embedding; q is rewritten in place, the
-// new k and the raw v are appended to the pages.
+// Fused Qwen3 prefill prologue, k and v side: per token and kv head, RMSNorm
+// of k over head_dim with a gain, then half-split rotary embedding, and the
+// new k and the raw v are appended to the pages.  (q gets the same norm and
+// rotation inside the prefill attention kernel, as it loads q.)
 //
 // Row layout: D/8 lanes hold one head row, 8 dims (16 bytes) each.  The
 // rotate_half partner of dims 8c..8c+7 lives in lane c ^ (D/16) of the same
 // row group, and the mean of squares is a xor-shuffle reduction over the
 // row's lanes.  All arithmetic is fp32; each output is rounded to bf16 once.
-// grid = (ceil(n_q/4) + ceil(n_kv/4) + n_kv, ceil(T / 64)): a workgroup
-// handles 64 tokens of up to 4 q heads, of up to 4 k heads, or of one v head
-// (the v heads stage V^T in LDS, as the append kernel does).
+// grid = (ceil(n_kv/4) + n_kv, ceil(T / 64)): a workgroup handles 64 tokens
+// of up to 4 k heads, or of one v head (the v heads stage V^T in LDS, as the
+// append kernel does).
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -17,7 +18,7 @@ namespace pkv {
 namespace {
 
 constexpr int kProTokens = 64;
-// q or k heads per workgroup (fewer at head_dim 256, for registers)
+// k heads per workgroup (fewer at head_dim 256, for registers)
 template <int D>
 constexpr int pro_heads() { return D >= 256 ? 2 : 4; }
 constexpr int kCuStage = 512;  // sequences whose metadata is staged in LDS (n_seqs < this)
@@ -99,7 +100,7 @@ struct ProSmem {
   bf16_t v[kProTokens][D + 2];  // +2: odd dword stride, no bank conflicts
 };
 
-enum { kHeadQ = 0, kHeadK = 1, kHeadV = 2 };
+enum { kHeadK = 1, kHeadV = 2 };
 
 // One workgroup: 64 tokens of one head of kind KIND (q: normalise + rotate in
 // place; k: normalise + rotate + append; v: raw append).  Each kind (and the
@@ -107,8 +108,8 @@ enum { kHeadQ = 0, kHeadK = 1, kHeadV = 2 };
 // waits for one path's loads never drain another's rows in flight.
 template <int D, int KIND, bool STAGED>
 __device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>& sm, int h0) {
-  // q / k workgroups take pro_heads<D>() heads of the same tokens (the cos /
-  // sin of a token serve all of them); v workgroups one head.
+  // k workgroups take pro_heads<D>() heads of the same tokens (the cos / sin
+  // of a token serve all of them); v workgroups one head.
   constexpr int LPR = D / 8;
   constexpr int ROWS = 256 / LPR;              // rows processed per pass by the workgroup
   constexpr int PASSES = kProTokens / ROWS;    // passes over the 64 tokens
@@ -119,7 +120,7 @@ __device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>&
   const int c = tid % LPR;
   const int rsub = tid / LPR;
   constexpr int HN = KIND == kHeadV ? 1 : pro_heads<D>();
-  const int n_heads = KIND == kHeadQ ? a.n_q : n_kv;  // heads of this kind
+  const int n_heads = n_kv;
   const int h = h0;  // first head of the workgroup
   // Sequence metadata (cu_seqlens, slots, start_pos) staged in LDS: loads
   // issued first, the row loads right after, so the set-up overlaps the rows'
@@ -137,8 +138,8 @@ __device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>&
   }
   // This thread's rows.  Rows past the last token re-read token t0 (in
   // bounds) and are never stored.
-  const bf16_t* src = KIND == kHeadQ ? a.q : (KIND == kHeadK ? a.k_raw : a.v_raw);
-  const int src_heads = KIND == kHeadQ ? a.n_q : n_kv;
+  const bf16_t* src = KIND == kHeadK ? a.k_raw : a.v_raw;
+  const int src_heads = n_kv;
   u32x4 x[PASSES][HN];
 #pragma unroll
   for (int k = 0; k < PASSES; ++k) {
@@ -177,7 +178,7 @@ __device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>&
     const int pos = sp + (t - cu_n);
     int page = -1, row = 0;
     const bool ok = slot > 0 && slot < a.pt.max_slots && pos >= 0 && pos < a.max_pos;
-    if (KIND != kHeadQ && ok) {  // q rows need only the position
+    if (ok) {
       const int lp = pos >> a.g.log2ps;
       if (lp < a.pt.pps) {
         const int pg = a.pt.table[(size_t)slot * a.pt.pps + lp];
@@ -239,7 +240,7 @@ __device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>&
       }
     }
   }
-  const bf16_t* w = KIND == kHeadQ ? a.q_w : a.k_w;
+  const bf16_t* w = a.k_w;
 #pragma unroll
   for (int k = 0; k < PASSES; ++k) {
     const int tt = rsub + k * ROWS;
@@ -248,34 +249,26 @@ __device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>&
     for (int j = 0; j < HN; ++j) {
       if (h + j >= n_heads) break;  // uniform over the workgroup
       const u32x4 y = norm_rope_row<D>(x[k][j], w, cs[k], sn[k], c, a.eps);
-      if (KIND == kHeadQ) {
-        store16(a.q + ((size_t)(t0 + tt) * a.n_q + h + j) * D + 8 * c, y);
-      } else if (sm.page[tt] >= 0) {
+      if (sm.page[tt] >= 0) {
         store16(a.kpool + (size_t)sm.page[tt] * page_stride + (h + j) * blk + (size_t)sm.row[tt] * D + 8 * c, y);
       }
     }
   }
 }
 
-// grid = (nq_wg + nk_wg + n_kv, ceil(T / 64)): x < nq_wg takes q heads
-// pro_heads<D>()*x .., then the k-head workgroups, then one per v head.
+// grid = (nk_wg + n_kv, ceil(T / 64)): x < nk_wg takes k heads
+// pro_heads*x .., then one workgroup per v head.
 template <int D>
 __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
   __shared__ ProSmem<D> sm;
-  const int nq_wg = (a.n_q + pro_heads<D>() - 1) / pro_heads<D>();
   const int nk_wg = (a.g.n_kv + pro_heads<D>() - 1) / pro_heads<D>();
   const int x = blockIdx.x;
-  const int kind = x < nq_wg ? kHeadQ : (x < nq_wg + nk_wg ? kHeadK : kHeadV);
-  const int h0 = kind == kHeadQ ? pro_heads<D>() * x
-               : (kind == kHeadK ? pro_heads<D>() * (x - nq_wg) : x - nq_wg - nk_wg);
   if (a.n_seqs < kCuStage) {
-    if (kind == kHeadQ) prologue_body<D, kHeadQ, true>(a, sm, h0);
-    else if (kind == kHeadK) prologue_body<D, kHeadK, true>(a, sm, h0);
-    else prologue_body<D, kHeadV, true>(a, sm, h0);
+    if (x < nk_wg) prologue_body<D, kHeadK, true>(a, sm, pro_heads<D>() * x);
+    else prologue_body<D, kHeadV, true>(a, sm, x - nk_wg);
   } else {
-    if (kind == kHeadQ) prologue_body<D, kHeadQ, false>(a, sm, h0);
-    else if (kind == kHeadK) prologue_body<D, kHeadK, false>(a, sm, h0);
-    else prologue_body<D, kHeadV, false>(a, sm, h0);
+    if (x < nk_wg) prologue_body<D, kHeadK, false>(a, sm, pro_heads<D>() * x);
+    else prologue_body<D, kHeadV, false>(a, sm, x - nk_wg);
   }
 }
 
@@ -284,9 +277,8 @@ hipError_t launch_prologue_d(const PrologueArgs& a, hipStream_t st) {
   // Heads vary fastest: the workgroups in flight cover all heads of a few
   // token blocks, i.e. contiguous [token][head][D] memory, not one head's
   // 256-byte pieces strided across many tokens.
-  const int nq_wg = (a.n_q + pro_heads<D>() - 1) / pro_heads<D>();
   const int nk_wg = (a.g.n_kv + pro_heads<D>() - 1) / pro_heads<D>();
-  dim3 grid(nq_wg + nk_wg + a.g.n_kv, (a.T + kProTokens - 1) / kProTokens);
+  dim3 grid(nk_wg + a.g.n_kv, (a.T + kProTokens - 1) / kProTokens);
   hipLaunchKernelGGL((prologue_kernel<D>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
