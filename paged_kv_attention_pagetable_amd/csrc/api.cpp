@@ -223,8 +223,8 @@ pkv_status pkv_attn_prefill(const void* q, int32_t n_q_heads, const int32_t* cu_
         !pro->v_raw)
       return fail(PKV_ERR_INVALID_ARG, "%s: NULL pointer in the prologue", fn);
     if (pro->max_pos < 1) return fail(PKV_ERR_INVALID_ARG, "%s: prologue max_pos must be >= 1", fn);
-    if ((total_tokens + 63) / 64 > 65535)
-      return fail(PKV_ERR_UNSUPPORTED, "%s: with the prologue, total_tokens must be <= 4194240", fn);
+    if ((total_tokens + 31) / 32 > 65535)
+      return fail(PKV_ERR_UNSUPPORTED, "%s: with the prologue, total_tokens must be <= 2097120", fn);
     if (!(pro->eps >= 0.f) || !std::isfinite(pro->eps))
       return fail(PKV_ERR_INVALID_ARG, "%s: prologue eps must be finite and >= 0", fn);
     pkv::PrologueArgs p;

@@ -7,9 +7,8 @@
 // rotate_half partner of dims 8c..8c+7 lives in lane c ^ (D/16) of the same
 // row group, and the mean of squares is a xor-shuffle reduction over the
 // row's lanes.  All arithmetic is fp32; each output is rounded to bf16 once.
-// grid = (ceil(n_kv/4) + n_kv, ceil(T / 64)): a workgroup handles 64 tokens
-// of up to 4 k heads, or of one v head (the v heads stage V^T in LDS, as the
-// append kernel does).
+// grid = (2 n_kv, ceil(T / 32)): a workgroup handles 32 tokens of one k head
+// or of one v head (the v heads stage V^T in LDS, as the append kernel does).
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -17,10 +16,12 @@ namespace pkv {
 
 namespace {
 
-constexpr int kProTokens = 64;
-// k heads per workgroup (fewer at head_dim 256, for registers)
+constexpr int kProTokens = 32;  // tokens per workgroup (many small workgroups: the
+                                 // per-workgroup set-up is latency, not bandwidth)
+// k heads per workgroup (one: more workgroups in flight measured faster than
+// sharing a token's cos / sin across heads)
 template <int D>
-constexpr int pro_heads() { return D >= 256 ? 2 : 4; }
+constexpr int pro_heads() { return 1; }
 constexpr int kCuStage = 512;  // sequences whose metadata is staged in LDS (n_seqs < this)
 
 // cs / sn: cos and sin of the lane's 8 rotary angles (frequencies f0 .. f0+7,
@@ -112,7 +113,7 @@ __device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>&
   // of a token serve all of them); v workgroups one head.
   constexpr int LPR = D / 8;
   constexpr int ROWS = 256 / LPR;              // rows processed per pass by the workgroup
-  constexpr int PASSES = kProTokens / ROWS;    // passes over the 64 tokens
+  constexpr int PASSES = kProTokens / ROWS;    // passes over the workgroup's tokens
   const int t0 = blockIdx.y * kProTokens;
   const int nt = min(kProTokens, a.T - t0);
   const int tid = threadIdx.x;

@@ -94,6 +94,10 @@ def test_append_and_prefill_argument_checks():
     bad = _lib.Prologue(None, 1, 1e-6, 1, 1, 16, 1, 1)
     assert L.pkv_attn_prefill(1, 4, 1, 1, None, 1, 8, 8, _pt(), ctypes.byref(cd), 1, 1, 0.1, 0,
                               ctypes.byref(bad), 1, None, None, 0, None) == 1
+    # the prologue's grid covers at most 65535 blocks of 32 tokens
+    good = _lib.Prologue(1, 1, 1e-6, 1, 1, 16, 1, 1)
+    assert L.pkv_attn_prefill(1, 4, 1, 1, None, 1, 2097121, 8, _pt(), ctypes.byref(cd), 1, 1,
+                              0.1, 0, ctypes.byref(good), 1, None, None, 0, None) == 2
     # prefill scale must be > 0
     assert L.pkv_attn_prefill(1, 4, 1, 1, None, 1, 8, 8, _pt(), ctypes.byref(cd), 1, 1,
                               -0.1, 0, None, 1, None, None, 0, None) == 1
