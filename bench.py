@@ -316,9 +316,11 @@ def _pmc_per_kernel(db_path, counter):
 
 
 PMC_PARTS = {
-    # part: (kernel-name key counted per call, sources whose hash the record keeps)
-    "decode": ("decode_", ["decode.hip", "pkv_device.h", "pkv_internal.h"]),
-    "prefill": ("prefill_kernel", ["prefill.hip", "pkv_device.h", "pkv_internal.h"]),
+    # part: (substrings a counted kernel's name contains, sources whose hash the
+    # record keeps).  Prefill counts the attention kernel without the fused q
+    # prologue: the instance the roofline times.
+    "decode": (("decode_",), ["decode.hip", "pkv_device.h", "pkv_internal.h"]),
+    "prefill": (("prefill_kernel<", ", false>"), ["prefill.hip", "pkv_device.h", "pkv_internal.h"]),
 }
 
 
@@ -344,11 +346,12 @@ def summarize_pmc(fetch_db, write_db, out_prefix, workload="qwen3_decode", comma
             continue
         fb = float(np.mean(fetch.get(k, [0.0]))) * 1024.0 * (f_scale or 1.0)
         wb = float(np.mean(write.get(k, [0.0]))) * 1024.0 * (w_scale or 1.0)
-        if key in k:
+        counted = all(part_key in k for part_key in key)
+        if counted:
             per_call += fb + wb
         short = k.replace("void ", "").replace("pkv::(anonymous namespace)::", "").split("(")[0]
         parts[short] = dict(fetch_bytes=round(fb), write_bytes=round(wb),
-                            dispatches=len(fetch.get(k, [])), counted=key in k)
+                            dispatches=len(fetch.get(k, [])), counted=counted)
     rec = dict(workload=workload, part=part, source_sha=source_sha(sources),
                hbm_bytes_per_call=round(per_call), kernels=parts,
                copy_scale=dict(fetch=f_scale, write=w_scale, copy_bytes=copy_bytes),
