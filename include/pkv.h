@@ -106,6 +106,10 @@ typedef struct {
   int32_t max_pos;
   const void* k_raw;      /* device bf16 [total_tokens][n_kv][head_dim] */
   const void* v_raw;      /* device bf16 [total_tokens][n_kv][head_dim] */
+  void* q_out;            /* device bf16 [total_tokens][n_q][head_dim] or NULL:
+                             where given, the normalised and rotated q' is
+                             also written there (rows of padding sequences and
+                             of positions >= max_pos are left untouched) */
 } pkv_prologue;
 
 /* ---------------------------------------------------------------------------

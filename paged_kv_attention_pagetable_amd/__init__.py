@@ -169,9 +169,10 @@ def attn_prefill(q, cu_seqlens, slots, table, k_pool, v_pool, scale=None, window
     """Packed varlen prefill attention; returns ``out [T, n_q, D]`` (bf16).
 
     ``prologue`` (optional) is a dict with ``q_norm_w, k_norm_w, eps, cos, sin,
-    k, v``: k (normalised and rotated) and v are appended before the
-    attention, and q is normalised and rotated inside the attention kernel
-    (``q`` itself is not modified).
+    k, v`` and optionally ``q_out``: k (normalised and rotated) and v are
+    appended before the attention, and q is normalised and rotated inside the
+    attention kernel (``q`` itself is not modified; the normalised q' is also
+    written to ``q_out`` when given).
     """
     cd, pt = _cache(k_pool, v_pool, table)
     _bits16(q, "q")
@@ -200,9 +201,14 @@ def attn_prefill(q, cu_seqlens, slots, table, k_pool, v_pool, scale=None, window
         if cos.dtype != torch.float32 or tuple(cos.shape[1:]) != (D // 2,) or \
                 sin.shape != cos.shape:
             raise ValueError("rope tables must be fp32 [max_pos, head_dim/2]")
+        q_out = p.get("q_out")
+        if q_out is not None:
+            _bits16(q_out, "q_out")
+            if tuple(q_out.shape) != (T, n_q, D):
+                raise ValueError("prologue q_out must be [T, n_q, head_dim]")
         pro = Prologue(p["q_norm_w"].data_ptr(), p["k_norm_w"].data_ptr(), float(p["eps"]),
                        cos.data_ptr(), sin.data_ptr(), cos.shape[0], p["k"].data_ptr(),
-                       p["v"].data_ptr())
+                       p["v"].data_ptr(), q_out.data_ptr() if q_out is not None else None)
     check(lib().pkv_attn_prefill(_ptr(q), n_q, _ptr(cu_seqlens), _ptr(slots), _ptr(start_pos),
                                  n_seqs, T, int(max_seqlen_q_hint), pt, ctypes.byref(cd),
                                  _ptr(k_pool), _ptr(v_pool), float(scale), int(window),

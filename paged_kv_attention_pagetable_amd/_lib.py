@@ -40,7 +40,7 @@ class PageTableRef(ctypes.Structure):
 class Prologue(ctypes.Structure):
     _fields_ = [("q_norm_w", c_void_p), ("k_norm_w", c_void_p), ("eps", c_float),
                 ("rope_cos", c_void_p), ("rope_sin", c_void_p), ("max_pos", c_int32),
-                ("k_raw", c_void_p), ("v_raw", c_void_p)]
+                ("k_raw", c_void_p), ("v_raw", c_void_p), ("q_out", c_void_p)]
 
 
 class PkvError(RuntimeError):

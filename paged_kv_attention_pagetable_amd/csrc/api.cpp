@@ -272,6 +272,7 @@ pkv_status pkv_attn_prefill(const void* q, int32_t n_q_heads, const int32_t* cu_
   a.sin_t = pro ? pro->rope_sin : nullptr;
   a.eps = pro ? pro->eps : 0.f;
   a.max_pos = pro ? pro->max_pos : 0;
+  a.q_out = pro ? static_cast<pkv::bf16_t*>(pro->q_out) : nullptr;
   return launched(pkv::launch_prefill(a, s), fn);
 }
 

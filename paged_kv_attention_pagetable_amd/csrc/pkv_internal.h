@@ -124,6 +124,7 @@ struct PrefillArgs {
   const float* sin_t;
   float eps;
   int max_pos;
+  bf16_t* q_out;  // optional copy of the transformed q' ([T][n_q][D])
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);

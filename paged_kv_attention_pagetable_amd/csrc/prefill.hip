@@ -204,6 +204,7 @@ struct WaveQ {
   u32x4 q[NT][D / 32];  // B operand of S^T = K Q^T (k-slot j of lane group g = dim 8g+j+32c)
   int pcol[NT];         // query position of the lane's column (-1: no query)
   int lo, hi;           // positions of the wave's first / last query (hi < 0: none)
+  bf16_t* qout_row[NT];  // this lane's 16-byte slot of the column's q' row (q_out only)
 };
 
 // Sum over the four lanes l, l^16, l^32, l^48 (the 4 dim groups of a column);
@@ -312,6 +313,10 @@ __device__ __forceinline__ void norm_rope_q(const PrefillArgs& a, int quad,
     for (int c = 0; c < C; ++c)
       wq.q[nt][c] = u32x4{pack_bf16x2(x[c][0], x[c][1]), pack_bf16x2(x[c][2], x[c][3]),
                           pack_bf16x2(x[c][4], x[c][5]), pack_bf16x2(x[c][6], x[c][7])};
+    if (a.q_out && wq.pcol[nt] < a.max_pos) {  // optional copy of q' (row of this column)
+#pragma unroll
+      for (int c = 0; c < C; ++c) store16(wq.qout_row[nt] + 32 * c, wq.q[nt][c]);
+    }
   }
 }
 
@@ -326,8 +331,9 @@ __device__ __forceinline__ void load_q(const PrefillArgs& a, const Item& it, int
     const int i = col / G, g = col - i * G;
     const bool valid = i < it.nq && !it.idle;
     wq.pcol[nt] = valid ? it.sp + it.i0 + i : -1;
-    const bf16_t* qrow =
-        a.q + ((size_t)(it.a0 + it.i0 + (valid ? i : 0)) * a.n_q + it.hk * G + g) * D + 8 * quad;
+    const size_t qoff = ((size_t)(it.a0 + it.i0 + (valid ? i : 0)) * a.n_q + it.hk * G + g) * D + 8 * quad;
+    const bf16_t* qrow = a.q + qoff;
+    wq.qout_row[nt] = a.q_out + qoff;  // (only dereferenced when q_out is given)
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
       const u32x4 v = load16(qrow + 32 * c);

@@ -7,7 +7,7 @@ import torch
 import oracle
 import paged_kv_attention_pagetable_amd as pkv
 from synth import CONFIGS, config_lengths, make_prefill_case
-from tests.gpu_util import (assert_attn_close, dev_bits, dev_i32, gpu_pools, host_bits,
+from tests.gpu_util import (DEV, assert_attn_close, dev_bits, dev_i32, gpu_pools, host_bits,
                             host_f64)
 
 pytestmark = pytest.mark.gpu
@@ -120,13 +120,14 @@ def test_prefill_long_prompt_sampled():
         assert np.max(np.abs(gl[t] - ref_lse)) <= 1e-3
 
 
-def _run_with_prologue(case, kp, vp, table, hint=None):
+def _run_with_prologue(case, kp, vp, table, hint=None, q_out=None):
     D = case.head_dim
     max_pos = int((case.start_pos + np.diff(case.cu_seqlens)).max()) + 1
     cos, sin = pkv.rope_table(max_pos, D, case.theta)
     q = dev_bits(case.q)
     pro = dict(q_norm_w=dev_bits(case.q_norm_w), k_norm_w=dev_bits(case.k_norm_w),
-               eps=case.eps, cos=cos, sin=sin, k=dev_bits(case.k), v=dev_bits(case.v))
+               eps=case.eps, cos=cos, sin=sin, k=dev_bits(case.k), v=dev_bits(case.v),
+               q_out=q_out)
     out = pkv.attn_prefill(q, dev_i32(case.cu_seqlens), dev_i32(case.slots), table, kp, vp,
                            scale=case.scale, window=case.window,
                            start_pos=dev_i32(case.start_pos),
@@ -146,10 +147,20 @@ def _oracle_with_prologue(case, okp, ovp):
 
 
 def _check_with_prologue(case, kp, vp, table, okp, ovp, name, hint=None):
-    q, out = _run_with_prologue(case, kp, vp, table, hint=hint)
+    # q' also copied out (q_out), over a sentinel fill
+    q_out = torch.full(case.q.shape, -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    q, out = _run_with_prologue(case, kp, vp, table, hint=hint, q_out=q_out)
     q2, q2b, k2 = _oracle_with_prologue(case, okp, ovp)
     # q is normalised and rotated inside the attention kernel, never written
     assert np.array_equal(host_bits(q), case.q), "q was modified"
+    # q': within tolerance of the fp64 value and (almost always) its nearest
+    # bf16; rows of padding sequences untouched
+    live = case.token_slots() != 0
+    gq = host_bits(q_out)
+    assert_attn_close(oracle.bf16_bits_to_f64(gq[live]), q2[live], "q'")
+    ulp_ok = np.mean(gq[live] == q2b[live])
+    assert ulp_ok >= 0.99, f"only {ulp_ok:.4f} of q' match the RNE-rounded fp64 value"
+    assert np.all(gq[~live] == 0xFFFF), "q' written for a padding sequence"
     # the K pool holds k' (within tolerance of the fp64 value, and almost
     # always its nearest bf16), the V pool the raw v bit for bit
     gk = host_bits(kp)
