@@ -226,6 +226,39 @@ pkv_status pkv_attn_prefill(const void* q, int32_t n_q_heads, const int32_t* cu_
 pkv_status pkv_rope_table(float* cos_out, float* sin_out, int32_t max_pos,
                           int32_t head_dim, double theta, void* stream);
 
+/* Bytes of workspace pkv_attn_prefill needs for these sizes: 0 (the prefill
+ * kernels use none; the workspace arguments are accepted for a stable ABI). */
+size_t pkv_prefill_workspace_size(int32_t total_tokens, int32_t n_seqs, int32_t n_q_heads);
+
+/* ---------------------------------------------------------------------------
+ * Validation mode (debugging aid).  The page table's entries, the slots and
+ * the lengths / positions live on the device, so the host checks above cannot
+ * see them; the pages leave an unmapped -1 entry unchecked
+ * ([continuous-batching compare] flex_paged_attention.py, PageTable.assign
+ * and the cache write).  With validation on, every pkv_append /
+ * pkv_attn_decode / pkv_attn_prefill first enqueues, on its stream, a check of
+ * the metadata it is about to use:
+ *   a slot outside [0, max_slots)                              PKV_VALIDATE_SLOT
+ *   a table entry outside [1, n_pages) for a logical page the
+ *   call uses (pages [0, ceil(len / page_size)) of each active
+ *   row / sequence; the page of each appended token)           PKV_VALIDATE_PAGE
+ *   a length or position < 0 or beyond pages_per_slot*page_size PKV_VALIDATE_POS
+ * Slot 0 rows and tokens are the reserved no-op and are never flagged.
+ * Findings are OR-ed into a flag word per device; the calls then run as
+ * usual (such inputs are handled as described at the top).  Validation is
+ * off by default; PKV_VALIDATE=1 in the environment switches it on at the
+ * first call, pkv_set_validation at any time (process-wide).
+ * pkv_validation_flags synchronises `stream`, writes the device's flag word
+ * to *flags (host memory) and, if `clear`, enqueues its reset to 0.  It
+ * returns PKV_ERR_INVALID_ARG for a NULL `flags`, PKV_ERR_LAUNCH if the copy
+ * fails.  The word is shared by every call on the device.
+ */
+#define PKV_VALIDATE_SLOT 1u
+#define PKV_VALIDATE_PAGE 2u
+#define PKV_VALIDATE_POS 4u
+pkv_status pkv_set_validation(int32_t on);
+pkv_status pkv_validation_flags(uint32_t* flags, int32_t clear, void* stream);
+
 /* Thread-local text of the last non-OK status returned on this thread. */
 const char* pkv_last_error(void);
 

@@ -26,6 +26,7 @@ from . import _lib
 from ._lib import CacheDesc, PageTableRef, Prologue, PkvError, check, lib
 
 __all__ = ["append", "attn_decode", "attn_prefill", "decode_workspace_size", "rope_table",
+           "set_validation", "validation_flags", "VALIDATE_SLOT", "VALIDATE_PAGE", "VALIDATE_POS",
            "new_pools", "v_pool_shape", "new_decode_workspace", "PageAllocator", "PkvError", "lib"]
 
 
@@ -215,6 +216,23 @@ def attn_prefill(q, cu_seqlens, slots, table, k_pool, v_pool, scale=None, window
                                  ctypes.byref(pro) if pro is not None else None, _ptr(out),
                                  _ptr(lse), None, 0, _stream(stream, q.device)))
     return out
+
+
+VALIDATE_SLOT, VALIDATE_PAGE, VALIDATE_POS = 1, 2, 4
+
+
+def set_validation(on=True):
+    """Switch validation mode on or off (process-wide; see the header)."""
+    check(lib().pkv_set_validation(1 if on else 0))
+
+
+def validation_flags(clear=True, stream=None, device=None):
+    """Synchronise the stream and return the device's validation flag word
+    (VALIDATE_SLOT | VALIDATE_PAGE | VALIDATE_POS bits), clearing it if asked."""
+    flags = ctypes.c_uint32(0)
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    check(lib().pkv_validation_flags(ctypes.byref(flags), 1 if clear else 0, _stream(stream, dev)))
+    return int(flags.value)
 
 
 class PageAllocator:

@@ -64,6 +64,9 @@ _SIGS = {
                                    c_size_t, c_void_p]),
     "pkv_rope_table": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, ctypes.c_double,
                                  c_void_p]),
+    "pkv_prefill_workspace_size": (c_size_t, [c_int32] * 3),
+    "pkv_set_validation": (c_int32, [c_int32]),
+    "pkv_validation_flags": (c_int32, [ctypes.POINTER(ctypes.c_uint32), c_int32, c_void_p]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
     "pkv_pt_create": (c_int32, [c_int32, c_int32, c_int32, ctypes.POINTER(c_void_p)]),

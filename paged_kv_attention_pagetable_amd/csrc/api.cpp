@@ -2,9 +2,11 @@
 // Nothing here allocates, frees or synchronises device memory.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "../../include/pkv.h"
@@ -79,9 +81,45 @@ pkv_status check_heads(const char* fn, int n_q, int n_kv, int* G) {
   return PKV_OK;
 }
 
+// Validation mode: off unless switched on by pkv_set_validation or by
+// PKV_VALIDATE=1 in the environment (read on first use).
+std::atomic<int> g_validate{-1};
+
+bool validation_on() {
+  int v = g_validate.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* e = std::getenv("PKV_VALIDATE");
+    v = (e && e[0] == '1') ? 1 : 0;
+    int expected = -1;
+    g_validate.compare_exchange_strong(expected, v);
+    v = g_validate.load(std::memory_order_relaxed);
+  }
+  return v == 1;
+}
+
 }  // namespace
 
 extern "C" {
+
+pkv_status pkv_set_validation(int32_t on) {
+  g_validate.store(on ? 1 : 0, std::memory_order_relaxed);
+  return PKV_OK;
+}
+
+pkv_status pkv_validation_flags(uint32_t* flags, int32_t clear, void* stream) {
+  const char* fn = "pkv_validation_flags";
+  if (!flags) return fail(PKV_ERR_INVALID_ARG, "%s: NULL output", fn);
+  const hipError_t e = pkv::read_validate_flags(flags, clear, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "%s: %s", fn, hipGetErrorString(e));
+  return PKV_OK;
+}
+
+size_t pkv_prefill_workspace_size(int32_t total_tokens, int32_t n_seqs, int32_t n_q_heads) {
+  (void)total_tokens;
+  (void)n_seqs;
+  (void)n_q_heads;
+  return 0;  // the prefill kernels use no workspace
+}
 
 const char* pkv_last_error(void) { return g_last_error.c_str(); }
 
@@ -109,6 +147,10 @@ pkv_status pkv_append(const void* k_new, const void* v_new, const int32_t* slot,
   a.g = g;
   a.kpool = static_cast<pkv::bf16_t*>(k_pool);
   a.vpool = static_cast<pkv::bf16_t*>(v_pool);
+  if (validation_on()) {
+    st = launched(pkv::launch_validate_tokens(tr, g, slot, pos, T, static_cast<hipStream_t>(stream)), fn);
+    if (st != PKV_OK) return st;
+  }
   return launched(pkv::launch_append(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -182,6 +224,12 @@ pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slot
   a.part_ml = plan.ws_bytes ? a.part_o + plan.part_o_floats : nullptr;
   a.out = static_cast<pkv::bf16_t*>(out);
   a.lse = lse;
+  if (validation_on()) {
+    st = launched(pkv::launch_validate_rows(tr, g, slots, seq_lens, nullptr, nullptr, B,
+                                            static_cast<hipStream_t>(stream)),
+                  fn);
+    if (st != PKV_OK) return st;
+  }
   return launched(pkv::launch_decode(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -218,6 +266,10 @@ pkv_status pkv_attn_prefill(const void* q, int32_t n_q_heads, const int32_t* cu_
   if (!q || !cu_seqlens || !slots || !k_pool || !v_pool || !out)
     return fail(PKV_ERR_INVALID_ARG, "%s: NULL tensor pointer", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validation_on()) {
+    st = launched(pkv::launch_validate_rows(tr, g, slots, nullptr, cu_seqlens, start_pos, n_seqs, s), fn);
+    if (st != PKV_OK) return st;
+  }
   if (pro) {
     if (!pro->q_norm_w || !pro->k_norm_w || !pro->rope_cos || !pro->rope_sin || !pro->k_raw ||
         !pro->v_raw)

@@ -127,6 +127,18 @@ struct PrefillArgs {
   bf16_t* q_out;  // optional copy of the transformed q' ([T][n_q][D])
 };
 
+// Validation mode flags (see pkv_validation_flags in the public header).
+constexpr uint32_t kValidateSlot = 1u;
+constexpr uint32_t kValidatePage = 2u;
+constexpr uint32_t kValidatePos = 4u;
+
+hipError_t launch_validate_rows(const TableRef& pt, const PoolGeom& g, const int32_t* slots,
+                                const int32_t* seq_lens, const int32_t* cu_seqlens,
+                                const int32_t* start_pos, int n, hipStream_t st);
+hipError_t launch_validate_tokens(const TableRef& pt, const PoolGeom& g, const int32_t* slot,
+                                  const int32_t* pos, int T, hipStream_t st);
+hipError_t read_validate_flags(uint32_t* host_out, int clear, hipStream_t st);
+
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t st);

@@ -104,6 +104,10 @@ def test_append_and_prefill_argument_checks():
     assert L.pkv_attn_prefill(1, 4, 1, 1, None, 1, 8, 8, _pt(), ctypes.byref(cd), 1, 1,
                               0.0, 0, None, 1, None, None, 0, None) == 1
     assert L.pkv_rope_table(None, 1, 8, 64, 1e6, None) == 1
+    # the prefill kernels need no workspace; validation-flag reads need an output
+    assert L.pkv_prefill_workspace_size(4096, 16, 32) == 0
+    assert L.pkv_validation_flags(None, 1, None) == 1
+    assert L.pkv_set_validation(0) == 0
     assert L.pkv_rope_table(1, 1, 8, 63, 1e6, None) == 1
 
 
