@@ -254,6 +254,20 @@ def time_graph(g, reps, warmup):
     return s.elapsed_time(e) / reps   # ms per replay
 
 
+def time_graph_each(g, reps):
+    """Per-replay times (ms) of `reps` back-to-back replays, one event pair each."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for s, e in ev:
+        s.record()
+        g.replay()
+        e.record()
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in ev]
+
+
 def source_sha(names):
     h = hashlib.sha256()
     for n in names:
@@ -357,6 +371,52 @@ def summarize_pmc(fetch_db, write_db, out_prefix, workload="qwen3_decode", comma
                copy_scale=dict(fetch=f_scale, write=w_scale, copy_bytes=copy_bytes),
                command=command)
     with open(out_prefix + ".json", "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_WAVES",
+                 "GRBM_GUI_ACTIVE"]
+N_CU, N_XCD = 256, 8
+FLOP_PER_MFMA = 16 * 16 * 32 * 2   # v_mfma_f32_16x16x32_bf16, one wave instruction
+
+
+def summarize_mfma(db_path, out_path, command=""):
+    """Matrix-core counters of the prefill attention kernel (the instance the
+    roofline times) from one `rocprofv3 --pmc` run: MFMA busy fraction of all
+    SIMD cycles (busy cycles over GRBM_GUI_ACTIVE per XCD x CUs x 4 SIMDs) and
+    MFMA FLOPs executed vs algorithmic."""
+    import sqlite3
+    db = sqlite3.connect(db_path)
+    key = "%prefill_kernel<%, false>%"
+    vals = {}
+    for c in MFMA_COUNTERS:
+        rows = db.execute("select dispatch_id, sum(counter_value) from pmc_events where name like ? "
+                          "and counter_name = ? group by dispatch_id", (key, c)).fetchall()
+        vals[c] = float(np.mean([r[1] for r in rows])) if rows else None
+    durs = [r[0] for r in db.execute("select duration from kernels where name like ?", (key,))]
+    dur_ns = float(np.mean(durs)) if durs else None
+    pw_flops = None
+    try:
+        from synth import CONFIGS, config_lengths
+        c = CONFIGS["qwen3_prefill"]
+        lengths, _ = config_lengths("qwen3_prefill")
+        pw_flops = int(sum(2 * c["head_dim"] * c["n_q"] * int(L) * (int(L) + 1) for L in lengths))
+    except Exception:  # pragma: no cover
+        pass
+    gui = vals.get("GRBM_GUI_ACTIVE")
+    busy = vals.get("SQ_VALU_MFMA_BUSY_CYCLES")
+    rec = dict(kernel="prefill_kernel<128, 2, false> (qwen3_prefill attention)",
+               source_sha=source_sha(PMC_PARTS["prefill"][1]), counters=vals,
+               kernel_ns_under_counters=dur_ns, command=command)
+    if gui and busy:
+        rec["mfma_busy_fraction"] = round(busy / (gui / N_XCD * N_CU * 4), 4)
+    if vals.get("SQ_INSTS_MFMA") and pw_flops:
+        executed = vals["SQ_INSTS_MFMA"] * FLOP_PER_MFMA
+        rec["mfma_flops_executed"] = executed
+        rec["algorithmic_flops"] = pw_flops
+        rec["executed_over_algorithmic"] = round(executed / pw_flops, 3)
+    with open(out_path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
 
@@ -471,12 +531,18 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "OUT"),
                     help="write HBM traffic per attention call from two rocprofv3 --pmc "
                          "runs (FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("DB", "OUT"),
+                    help="write the prefill kernel's matrix-core counters from one rocprofv3 "
+                         "--pmc run and exit")
     ap.add_argument("--pmc-part", default="decode", choices=sorted(PMC_PARTS),
                     help="which attention kernel --summarize-pmc counts per call")
     ap.add_argument("--command", default="", help="command line recorded in summaries")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, command=args.command)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma, command=args.command)
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, workload=args.workload, command=args.command,
@@ -502,6 +568,7 @@ def main():
     log("timing decode step")
     torch.cuda.synchronize()
     ms_step = time_graph(g_step, args.steps, args.warmup)
+    each = time_graph_each(g_step, args.steps)
     ms_attn = time_graph(g_attn, args.kernel_reps, 2) / wl.n_calls
     attn_bytes = [wl.attn_bytes(ly) for ly in wl.layers]
     step_bytes = sum(attn_bytes) + sum(wl.append_bytes(ly) for ly in wl.layers)
@@ -519,6 +586,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16, random page permutation)",
         "config": wl.describe(), "roofline": roofline,
+        "step_ms_median": round(float(np.median(each)), 4), "step_ms_best": round(min(each), 4),
     }
     del g_step, g_attn
     if args.calibrate_copy:
@@ -536,11 +604,14 @@ def main():
         gp_attn = capture(pw.attn_only)
         log("timing prefill")
         ms_p = time_graph(gp_step, args.steps, args.warmup)
+        each_p = time_graph_each(gp_step, args.steps)
         ms_pa = time_graph(gp_attn, args.kernel_reps, 2) / pw.n_calls
         fl = pw.flops_per_call()
         tflops = fl / (ms_pa * 1e-3) / 1e12
         result["prefill"] = {
             "config": pw.describe(), "ms_per_step": round(ms_p, 4),
+            "step_ms_median": round(float(np.median(each_p)), 4),
+            "step_ms_best": round(min(each_p), 4),
             "tflops_step": round(fl * pw.n_calls / (ms_p * 1e-3) / 1e12, 2),
             "roofline": dict(bound="mfma", achieved=round(tflops, 2),
                              peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
