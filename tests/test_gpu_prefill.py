@@ -208,6 +208,33 @@ def test_prefill_with_prologue_staged_metadata_boundary():
     _check_with_prologue(case, kp, vp, table, okp, ovp, "511 prompts")
 
 
+# Mixed prefill + decode in one launch: decode rows are 1-token sequences
+# whose start_pos is their cached length (the new token's position), beside
+# prompts with and without a cached prefix.
+MIXED_LENGTHS = [40, 1, 100, 1, 1, 7, 1, 1]
+MIXED_START = [0, 63, 30, 200, 511, 0, 0, 1000]
+
+
+def test_mixed_prefill_and_decode_rows_in_one_launch():
+    case = make_prefill_case(8, 2, 128, 64, MIXED_LENGTHS, seed=2500, start_pos=MIXED_START)
+    kp, vp, table, okp, ovp = _pools_with_prefix(case)
+    _append_tokens(case, kp, vp, table, okp, ovp)
+    q, out, lse = _run_no_prologue(case, kp, vp, table)
+    _check_no_prologue(case, q, out, lse, okp, ovp, "mixed")
+    # the 1-token rows are exactly decode steps: same result as the decode oracle
+    dec = [n for n, L in enumerate(MIXED_LENGTHS) if L == 1]
+    tok = case.cu_seqlens[dec]
+    ref_d, _ = oracle.attn_decode(case.q[tok], okp, ovp, case.table, case.slots[dec],
+                                  case.start_pos[dec] + 1, case.scale)
+    assert_attn_close(host_f64(out)[tok], ref_d, "decode rows")
+
+
+def test_mixed_prefill_and_decode_rows_with_prologue():
+    case = make_prefill_case(8, 2, 128, 64, MIXED_LENGTHS, seed=2501, start_pos=MIXED_START)
+    kp, vp, table, okp, ovp = _pools_with_prefix(case)
+    _check_with_prologue(case, kp, vp, table, okp, ovp, "mixed with prologue")
+
+
 def test_rope_table_matches_fp64():
     D, theta, max_pos = 128, 1e6, 4096
     c, s = pkv.rope_table(max_pos, D, theta)
