@@ -11,7 +11,8 @@ written as the plain definition of what the pages describe:
 * ``paged``     -- page-table addressing, the append scatter, page gather and
                    textbook masked-softmax GQA attention for decode and packed
                    varlen prefill (causal / sliding-window / document masks).
-* ``prologue``  -- per-head RMSNorm followed by half-split rotary embedding.
+* ``prologue``  -- per-head RMSNorm followed by half-split rotary embedding
+                   (Qwen3; Gemma-4 with v_norm, K=V and partial rotary).
 * ``pagetable`` -- the host-side slot / page allocator state machine.
 
 Pages cited (by title / address; a section is a file shown on that page):
@@ -40,5 +41,6 @@ from .paged import (  # noqa: F401
     attn_decode,
     attn_prefill,
 )
-from .prologue import rmsnorm, rope_inv_freq, rope_apply, prologue_qwen3  # noqa: F401
+from .prologue import (rmsnorm, rope_inv_freq, rope_inv_freq_partial, rope_apply,  # noqa: F401
+                       prologue_qwen3, prologue_gemma4)
 from .pagetable import PageTableModel  # noqa: F401

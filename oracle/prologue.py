@@ -1,4 +1,4 @@
-"""Oracle: the Qwen3 attention prologue (per-head q/k RMSNorm, then RoPE).
+"""Oracle: the Qwen3 and Gemma-4 attention prologues (per-head RMSNorm, then RoPE).
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  numpy float64.
 
@@ -43,6 +43,24 @@ def rope_inv_freq(head_dim: int, theta: float):
     return theta ** (-2.0 * i / head_dim)
 
 
+def rope_inv_freq_partial(head_dim: int, theta: float, rotary_fraction: float):
+    """Partial ("proportional") rotary frequencies of the Gemma-4 full layers.
+
+    [moe-qwen3 compare] flex_gemma4_moe.py (model notes, "Two-tier RoPE", and
+    the ``_apply_rotary_full`` docstring): only the leading
+    ``rotary_fraction`` of the frequencies rotate; the tail entries of
+    ``inv_freq`` are zero, so their cos = 1, sin = 0 and ``rotate_half`` over
+    the full head_dim passes those dims through.  Reading taken where the
+    pages are silent: the rotating frequencies keep the default exponents
+    over the full head_dim, ``theta ** (-2i / D)`` for
+    ``i < round(rotary_fraction * D / 2)``.
+    """
+    inv = rope_inv_freq(head_dim, theta)
+    n_rot = int(round(rotary_fraction * (head_dim // 2)))
+    inv[n_rot:] = 0.0
+    return inv
+
+
 def rope_apply(x, pos, inv_freq):
     """Half-split rotary embedding of ``x [..., D]`` at integer positions ``pos``.
 
@@ -72,3 +90,26 @@ def prologue_qwen3(q, k, v, q_norm_w, k_norm_w, positions, eps: float, theta: fl
     q2 = rope_apply(rmsnorm(qf, wq, eps), pos, inv)
     k2 = rope_apply(rmsnorm(kf, wk, eps), pos, inv)
     return q2, k2, vf
+
+
+def prologue_gemma4(q, k, v, q_norm_w, k_norm_w, positions, eps: float, theta: float,
+                    rotary_fraction: float = 1.0, k_eq_v: bool = False):
+    """The Gemma-4 attention prologue ([moe-qwen3 compare] flex_gemma4_moe.py,
+    attention forward and model notes 3-4): q and k get RMSNorm with their
+    gains, v gets RMSNorm without a gain (``v_norm``, ``with_scale=False``);
+    with K=V the value is the raw k projection (before ``k_norm`` and
+    rotary), then ``v_norm``.  q and k are then rotated (``rotary_fraction``
+    < 1: the full layers' partial RoPE).  Same bit-pattern inputs as
+    ``prologue_qwen3``; ``v`` is ignored when ``k_eq_v``.  Returns float64
+    ``(q', k', v')``.
+    """
+    qf, kf = bf16_bits_to_f64(q), bf16_bits_to_f64(k)
+    vf = kf if k_eq_v else bf16_bits_to_f64(v)
+    wq, wk = bf16_bits_to_f64(q_norm_w), bf16_bits_to_f64(k_norm_w)
+    D = qf.shape[-1]
+    inv = rope_inv_freq_partial(D, theta, rotary_fraction)
+    pos = np.asarray(positions, dtype=np.float64)[:, None]
+    q2 = rope_apply(rmsnorm(qf, wq, eps), pos, inv)
+    k2 = rope_apply(rmsnorm(kf, wk, eps), pos, inv)
+    v2 = rmsnorm(vf, 1.0, eps)
+    return q2, k2, v2

@@ -114,3 +114,73 @@ def test_prologue_composition_and_v_passthrough():
     kn = oracle.rmsnorm(oracle.bf16_bits_to_f64(case.k[t]),
                         oracle.bf16_bits_to_f64(case.k_norm_w), case.eps)
     assert np.max(np.abs(back - kn)) <= 1e-12
+
+
+# ------------------------------------------------------------ Gemma-4 ----
+
+def test_partial_rotary_frequencies_and_passthrough():
+    """Partial rotary: the leading fraction of the frequencies rotates, the
+    rest (zero inv_freq) passes through; closed forms at D = 16."""
+    D, theta = 16, 100.0
+    inv = oracle.rope_inv_freq_partial(D, theta, 0.25)
+    # round(0.25 * 8) = 2 rotating frequencies: 1 and theta^(-2/16)
+    assert inv[0] == 1.0 and abs(inv[1] - theta ** (-0.125)) <= 1e-15
+    assert np.all(inv[2:] == 0.0)
+    x = np.arange(1, D + 1, dtype=np.float64)
+    pos = 3
+    y = oracle.rope_apply(x, pos, inv)
+    # dims 2..7 and 10..15 are untouched
+    keep = np.r_[2:8, 10:16]
+    assert np.array_equal(y[keep], x[keep])
+    # pairs (0, 8) and (1, 9) are 2x2 rotations by pos * inv_i
+    for i in range(2):
+        a = pos * inv[i]
+        lo, hi = x[i], x[i + 8]
+        assert abs(y[i] - (lo * math.cos(a) - hi * math.sin(a))) <= 1e-12
+        assert abs(y[i + 8] - (hi * math.cos(a) + lo * math.sin(a))) <= 1e-12
+    # fraction 1 is the default table
+    assert np.array_equal(oracle.rope_inv_freq_partial(D, theta, 1.0),
+                          oracle.rope_inv_freq(D, theta))
+
+
+def test_gemma4_v_norm_k_eq_v_and_qk_match_qwen3():
+    from synth import make_prefill_case
+    case = make_prefill_case(4, 2, 32, 8, [5, 3], seed=19, start_pos=[0, 4], theta=1e4)
+    args = (case.q, case.k, case.v, case.q_norm_w, case.k_norm_w, case.token_pos(), case.eps,
+            case.theta)
+    q2, k2, v2 = oracle.prologue_gemma4(*args)
+    qq, kq, _ = oracle.prologue_qwen3(*args)
+    # with full rotary, q' and k' are the Qwen3 prologue's
+    assert np.array_equal(q2, qq) and np.array_equal(k2, kq)
+    # v_norm has no gain: v' = v / sqrt(mean(v^2) + eps), i.e. a positive
+    # multiple of v per row whose mean square is ms / (ms + eps)
+    v = oracle.bf16_bits_to_f64(case.v)
+    ms = np.mean(v * v, axis=-1, keepdims=True)
+    assert np.max(np.abs(np.mean(v2 * v2, axis=-1, keepdims=True) - ms / (ms + case.eps))) <= 1e-12
+    ratio = v2 / v
+    assert np.all(ratio > 0)
+    assert np.max(np.abs(ratio - ratio[..., :1])) <= 1e-12
+    # K=V: the value is v_norm of the raw k (the v argument is ignored)
+    _, k3, v3 = oracle.prologue_gemma4(*args, k_eq_v=True)
+    junk = np.zeros_like(case.v)
+    _, _, v4 = oracle.prologue_gemma4(case.q, case.k, junk, *args[3:], k_eq_v=True)
+    kraw = oracle.bf16_bits_to_f64(case.k)
+    assert np.array_equal(v3, v4)
+    assert np.max(np.abs(v3 - kraw / np.sqrt(np.mean(kraw * kraw, axis=-1, keepdims=True)
+                                             + case.eps))) <= 1e-15
+    assert np.array_equal(k3, k2)
+
+
+def test_gemma4_partial_rotary_keeps_tail_and_norm():
+    from synth import make_prefill_case
+    case = make_prefill_case(4, 2, 64, 8, [6], seed=23, start_pos=[9], theta=1e6)
+    q2, k2, _ = oracle.prologue_gemma4(case.q, case.k, case.v, case.q_norm_w, case.k_norm_w,
+                                       case.token_pos(), case.eps, case.theta,
+                                       rotary_fraction=0.25)
+    qn = oracle.rmsnorm(oracle.bf16_bits_to_f64(case.q), oracle.bf16_bits_to_f64(case.q_norm_w),
+                        case.eps)
+    # 8 of 32 frequencies rotate: dims 8..31 and 40..63 are the normed values
+    tail = np.r_[8:32, 40:64]
+    assert np.max(np.abs(q2[..., tail] - qn[..., tail])) <= 1e-15
+    # a rotation keeps each row's norm
+    assert np.max(np.abs(np.linalg.norm(q2, axis=-1) - np.linalg.norm(qn, axis=-1))) <= 1e-12
