@@ -86,13 +86,16 @@ typedef struct {
   int32_t pages_per_slot; /* row stride, in entries                           */
 } pkv_page_table;
 
-/* Fused Qwen3 prologue for prefill: per token and head,
+/* Fused attention prologue for prefill (Qwen3; Gemma-4 with v_norm): per
+ * token and head,
  *   x <- RMSNorm(x) * w  over head_dim  (fp32: x / sqrt(mean(x^2) + eps) * w)
  *   x <- x * cos + rotate_half(x) * sin, rotate_half(x) = (-x[D/2:], x[:D/2])
- * applied to k, which is then appended to the pages with the raw v, and to q
- * inside the attention kernel as it loads q (q in memory is not modified).  Order and formulas: [moe-qwen3 compare]
- * unsloth/inference/flex_gemma4_moe.py, attention forward (q_norm / k_norm,
- * then rotary, then the paged-KV write) and _rotate_half / _apply_rotary_full.
+ * applied to k, which is then appended to the pages with v (raw, or with
+ * v_norm its RMSNorm without a gain), and to q inside the attention kernel as
+ * it loads q (q in memory is not modified).  Order and formulas:
+ * [moe-qwen3 compare] unsloth/inference/flex_gemma4_moe.py, attention
+ * forward (q_norm / k_norm / v_norm, then rotary, then the paged-KV write)
+ * and _rotate_half / _apply_rotary_full.
  * The cos/sin tables are fp32 [max_pos][head_dim/2] (see pkv_rope_table); a
  * token at position p uses row p.  Positions >= max_pos are a caller error:
  * such a token's k is not appended and its q reads row max_pos-1 (in bounds;
@@ -110,6 +113,10 @@ typedef struct {
                              where given, the normalised and rotated q' is
                              also written there (rows of padding sequences and
                              of positions >= max_pos are left untouched) */
+  int32_t v_norm;         /* 0: v appended raw (Qwen3); 1: v <- RMSNorm(v)
+                             without a gain before the append (Gemma-4
+                             v_norm).  For Gemma-4's K=V layers pass the raw
+                             k as v_raw. */
 } pkv_prologue;
 
 /* ---------------------------------------------------------------------------
@@ -225,6 +232,18 @@ pkv_status pkv_attn_prefill(const void* q, int32_t n_q_heads, const int32_t* cu_
  */
 pkv_status pkv_rope_table(float* cos_out, float* sin_out, int32_t max_pos,
                           int32_t head_dim, double theta, void* stream);
+
+/* pkv_rope_table_partial -- the same with only the leading rotary_fraction of
+ * the head_dim/2 frequencies rotating: i < round(rotary_fraction * head_dim/2)
+ * use theta^(-2i/head_dim), the rest have a zero frequency (cos 1, sin 0), so
+ * the prologue's full-head rotate_half passes those dims through.  This is
+ * the "proportional" partial RoPE of the Gemma-4 full-attention layers
+ * ([moe-qwen3 compare] flex_gemma4_moe.py, model notes "Two-tier RoPE" and
+ * _apply_rotary_full).  rotary_fraction in (0, 1]; 1 = pkv_rope_table.
+ */
+pkv_status pkv_rope_table_partial(float* cos_out, float* sin_out, int32_t max_pos,
+                                  int32_t head_dim, double theta, double rotary_fraction,
+                                  void* stream);
 
 /* Bytes of workspace pkv_attn_prefill needs for these sizes: 0 (the prefill
  * kernels use none; the workspace arguments are accepted for a stable ABI). */

@@ -155,12 +155,14 @@ def new_decode_workspace(nbytes, device="cuda"):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def rope_table(max_pos, head_dim, theta, device="cuda", stream=None):
-    """fp32 ``cos, sin [max_pos, head_dim/2]`` of the default rope frequencies."""
+def rope_table(max_pos, head_dim, theta, device="cuda", stream=None, rotary_fraction=1.0):
+    """fp32 ``cos, sin [max_pos, head_dim/2]`` of the default rope frequencies
+    (``rotary_fraction < 1``: only that leading fraction rotates, the rest
+    pass through -- Gemma-4's partial RoPE)."""
     c = torch.empty((max_pos, head_dim // 2), dtype=torch.float32, device=device)
     s = torch.empty_like(c)
-    check(lib().pkv_rope_table(_ptr(c), _ptr(s), max_pos, head_dim, float(theta),
-                               _stream(stream, c.device)))
+    check(lib().pkv_rope_table_partial(_ptr(c), _ptr(s), max_pos, head_dim, float(theta),
+                                       float(rotary_fraction), _stream(stream, c.device)))
     return c, s
 
 
@@ -170,8 +172,9 @@ def attn_prefill(q, cu_seqlens, slots, table, k_pool, v_pool, scale=None, window
     """Packed varlen prefill attention; returns ``out [T, n_q, D]`` (bf16).
 
     ``prologue`` (optional) is a dict with ``q_norm_w, k_norm_w, eps, cos, sin,
-    k, v`` and optionally ``q_out``: k (normalised and rotated) and v are
-    appended before the attention, and q is normalised and rotated inside the
+    k, v`` and optionally ``q_out`` and ``v_norm`` (Gemma-4: v gets RMSNorm
+    without a gain; for K=V layers pass the raw k as ``v``): k (normalised and
+    rotated) and v are appended before the attention, and q is normalised and rotated inside the
     attention kernel (``q`` itself is not modified; the normalised q' is also
     written to ``q_out`` when given).
     """
@@ -209,7 +212,8 @@ def attn_prefill(q, cu_seqlens, slots, table, k_pool, v_pool, scale=None, window
                 raise ValueError("prologue q_out must be [T, n_q, head_dim]")
         pro = Prologue(p["q_norm_w"].data_ptr(), p["k_norm_w"].data_ptr(), float(p["eps"]),
                        cos.data_ptr(), sin.data_ptr(), cos.shape[0], p["k"].data_ptr(),
-                       p["v"].data_ptr(), q_out.data_ptr() if q_out is not None else None)
+                       p["v"].data_ptr(), q_out.data_ptr() if q_out is not None else None,
+                       1 if p.get("v_norm") else 0)
     check(lib().pkv_attn_prefill(_ptr(q), n_q, _ptr(cu_seqlens), _ptr(slots), _ptr(start_pos),
                                  n_seqs, T, int(max_seqlen_q_hint), pt, ctypes.byref(cd),
                                  _ptr(k_pool), _ptr(v_pool), float(scale), int(window),

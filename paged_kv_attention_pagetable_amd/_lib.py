@@ -40,7 +40,8 @@ class PageTableRef(ctypes.Structure):
 class Prologue(ctypes.Structure):
     _fields_ = [("q_norm_w", c_void_p), ("k_norm_w", c_void_p), ("eps", c_float),
                 ("rope_cos", c_void_p), ("rope_sin", c_void_p), ("max_pos", c_int32),
-                ("k_raw", c_void_p), ("v_raw", c_void_p), ("q_out", c_void_p)]
+                ("k_raw", c_void_p), ("v_raw", c_void_p), ("q_out", c_void_p),
+                ("v_norm", c_int32)]
 
 
 class PkvError(RuntimeError):
@@ -64,6 +65,8 @@ _SIGS = {
                                    c_size_t, c_void_p]),
     "pkv_rope_table": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, ctypes.c_double,
                                  c_void_p]),
+    "pkv_rope_table_partial": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, ctypes.c_double,
+                                         ctypes.c_double, c_void_p]),
     "pkv_prefill_workspace_size": (c_size_t, [c_int32] * 3),
     "pkv_set_validation": (c_int32, [c_int32]),
     "pkv_validation_flags": (c_int32, [ctypes.POINTER(ctypes.c_uint32), c_int32, c_void_p]),

@@ -283,6 +283,7 @@ pkv_status pkv_attn_prefill(const void* q, int32_t n_q_heads, const int32_t* cu_
     p.k_raw = static_cast<const pkv::bf16_t*>(pro->k_raw);
     p.v_raw = static_cast<const pkv::bf16_t*>(pro->v_raw);
     p.k_w = static_cast<const pkv::bf16_t*>(pro->k_norm_w);
+    p.v_norm = pro->v_norm ? 1 : 0;
     p.eps = pro->eps;
     p.cos_t = pro->rope_cos;
     p.sin_t = pro->rope_sin;
@@ -328,17 +329,26 @@ pkv_status pkv_attn_prefill(const void* q, int32_t n_q_heads, const int32_t* cu_
   return launched(pkv::launch_prefill(a, s), fn);
 }
 
-pkv_status pkv_rope_table(float* cos_out, float* sin_out, int32_t max_pos, int32_t head_dim,
-                          double theta, void* stream) {
+pkv_status pkv_rope_table_partial(float* cos_out, float* sin_out, int32_t max_pos,
+                                  int32_t head_dim, double theta, double rotary_fraction,
+                                  void* stream) {
   const char* fn = "pkv_rope_table";
   if (!cos_out || !sin_out) return fail(PKV_ERR_INVALID_ARG, "%s: NULL output", fn);
   if (max_pos < 1 || head_dim < 2 || head_dim % 2)
     return fail(PKV_ERR_INVALID_ARG, "%s: need max_pos >= 1 and an even head_dim >= 2", fn);
   if (!(theta > 0.0) || !std::isfinite(theta))
     return fail(PKV_ERR_INVALID_ARG, "%s: theta must be finite and > 0", fn);
-  return launched(pkv::launch_rope_table(cos_out, sin_out, max_pos, head_dim, theta,
+  if (!(rotary_fraction > 0.0 && rotary_fraction <= 1.0))
+    return fail(PKV_ERR_INVALID_ARG, "%s: rotary_fraction must be in (0, 1]", fn);
+  const int n_rot = (int)std::lround(rotary_fraction * (head_dim / 2));
+  return launched(pkv::launch_rope_table(cos_out, sin_out, max_pos, head_dim, theta, n_rot,
                                          static_cast<hipStream_t>(stream)),
                   fn);
+}
+
+pkv_status pkv_rope_table(float* cos_out, float* sin_out, int32_t max_pos, int32_t head_dim,
+                          double theta, void* stream) {
+  return pkv_rope_table_partial(cos_out, sin_out, max_pos, head_dim, theta, 1.0, stream);
 }
 
 }  // extern "C"

@@ -84,6 +84,7 @@ struct PrologueArgs {
   const bf16_t* k_raw;
   const bf16_t* v_raw;
   const bf16_t* k_w;
+  int v_norm;  // 1: v <- RMSNorm(v) without a gain before the append
   float eps;
   const float* cos_t;
   const float* sin_t;
@@ -144,7 +145,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_rope_table(float* c, float* s, int max_pos, int head_dim, double theta,
-                             hipStream_t st);
+                             int n_rot, hipStream_t st);
 
 // Split-K plan for decode (host): keys per split and grid extent.
 struct DecodePlan {

@@ -1,6 +1,7 @@
-// Fused Qwen3 prefill prologue, k and v side: per token and kv head, RMSNorm
-// of k over head_dim with a gain, then half-split rotary embedding, and the
-// new k and the raw v are appended to the pages.  (q gets the same norm and
+// Fused prefill prologue, k and v side: per token and kv head, RMSNorm of k
+// over head_dim with a gain, then half-split rotary embedding; the new k and
+// v (raw, or for Gemma-4 its RMSNorm without a gain) are appended to the
+// pages.  (q gets the same norm and
 // rotation inside the prefill attention kernel, as it loads q.)
 //
 // Row layout: D/8 lanes hold one head row, 8 dims (16 bytes) each.  The
@@ -23,6 +24,30 @@ constexpr int kProTokens = 32;  // tokens per workgroup (many small workgroups: 
 template <int D>
 constexpr int pro_heads() { return 1; }
 constexpr int kCuStage = 512;  // sequences whose metadata is staged in LDS (n_seqs < this)
+
+// RMSNorm without a gain of one head row (D/8 lanes, 8 dims each): the mean
+// of squares is a xor-shuffle sum over the row's lanes; fp32, one bf16
+// rounding (Gemma-4 v_norm).
+template <int D>
+__device__ __forceinline__ u32x4 norm_row(u32x4 x, float eps) {
+  constexpr int LPR = D / 8;
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = bf16lo(x[e]);
+    v[2 * e + 1] = bf16hi(x[e]);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) ss += shfl_xor(ss, m);
+  const float inv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+  u32x4 out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(v[2 * e] * inv, v[2 * e + 1] * inv);
+  return out;
+}
 
 // cs / sn: cos and sin of the lane's 8 rotary angles (frequencies f0 .. f0+7,
 // f0 = 8c mod D/2) at the row's position.
@@ -197,16 +222,17 @@ __device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>&
   const size_t blk = (size_t)ps * D;
   const size_t page_stride = (size_t)n_kv * blk;
   if (KIND == kHeadV) {
-    // raw V rows -> LDS staging, then stored transposed: lanes on
-    // consecutive tokens, so tokens sharing a page and key group are
-    // contiguous
+    // V rows (raw, or RMSNorm without a gain) -> LDS staging, then stored
+    // transposed: lanes on consecutive tokens, so tokens sharing a page and
+    // key group are contiguous
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
       const int tt = rsub + k * ROWS;
+      const u32x4 y = a.v_norm ? norm_row<D>(x[k][0], a.eps) : x[k][0];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sm.v[tt][8 * c + 2 * e] = (bf16_t)(x[k][0][e] & 0xffffu);
-        sm.v[tt][8 * c + 2 * e + 1] = (bf16_t)(x[k][0][e] >> 16);
+        sm.v[tt][8 * c + 2 * e] = (bf16_t)(y[e] & 0xffffu);
+        sm.v[tt][8 * c + 2 * e + 1] = (bf16_t)(y[e] >> 16);
       }
     }
     lds_barrier();
@@ -286,12 +312,13 @@ hipError_t launch_prologue_d(const PrologueArgs& a, hipStream_t st) {
 
 // cos / sin of p * theta^(-2i/D) in fp64, stored as fp32.
 __global__ void rope_table_kernel(float* c, float* s, int max_pos, int half, double theta,
-                                  int head_dim) {
+                                  int head_dim, int n_rot) {
   const long n = (long)max_pos * half;
   for (long idx = blockIdx.x * (long)blockDim.x + threadIdx.x; idx < n;
        idx += (long)gridDim.x * blockDim.x) {
     const int p = (int)(idx / half), i = (int)(idx - (long)p * half);
-    const double inv = pow(theta, -2.0 * (double)i / (double)head_dim);
+    // frequencies past n_rot are zero (partial rotary: cos 1, sin 0)
+    const double inv = i < n_rot ? pow(theta, -2.0 * (double)i / (double)head_dim) : 0.0;
     const double ang = (double)p * inv;
     c[idx] = (float)cos(ang);
     s[idx] = (float)sin(ang);
@@ -311,13 +338,13 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_rope_table(float* c, float* s, int max_pos, int head_dim, double theta,
-                             hipStream_t st) {
+                             int n_rot, hipStream_t st) {
   const int half = head_dim / 2;
   const long n = (long)max_pos * half;
   if (n <= 0) return hipSuccess;
   const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
   hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, st, c, s, max_pos, half,
-                     theta, head_dim);
+                     theta, head_dim, n_rot);
   return hipGetLastError();
 }
 

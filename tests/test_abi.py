@@ -109,6 +109,8 @@ def test_append_and_prefill_argument_checks():
     assert L.pkv_validation_flags(None, 1, None) == 1
     assert L.pkv_set_validation(0) == 0
     assert L.pkv_rope_table(1, 1, 8, 63, 1e6, None) == 1
+    assert L.pkv_rope_table_partial(1, 1, 8, 64, 1e6, 0.0, None) == 1   # fraction in (0, 1]
+    assert L.pkv_rope_table_partial(1, 1, 8, 64, 1e6, 1.5, None) == 1
 
 
 def test_cpp_allocator_follows_golden_sequence():

@@ -235,6 +235,58 @@ def test_mixed_prefill_and_decode_rows_with_prologue():
     _check_with_prologue(case, kp, vp, table, okp, ovp, "mixed with prologue")
 
 
+def test_rope_table_partial_matches_fp64():
+    D, theta, max_pos = 512, 1e6, 1024
+    c, s = pkv.rope_table(max_pos, D, theta, rotary_fraction=0.25)
+    torch.cuda.synchronize()
+    inv = oracle.rope_inv_freq_partial(D, theta, 0.25)
+    ang = np.arange(max_pos)[:, None] * inv[None, :]
+    assert np.max(np.abs(c.cpu().numpy() - np.cos(ang))) <= 1e-7
+    assert np.max(np.abs(s.cpu().numpy() - np.sin(ang))) <= 1e-7
+    assert np.all(c.cpu().numpy()[:, 64:] == 1.0) and np.all(s.cpu().numpy()[:, 64:] == 0.0)
+
+
+# Gemma-4 prologue variants: sliding layers (theta 1e4, window 64 here),
+# v_norm (RMSNorm without a gain) on v, K=V, and partial rotary.
+@pytest.mark.parametrize("k_eq_v,fraction", [(False, 1.0), (True, 1.0), (True, 0.25)])
+def test_prefill_with_gemma4_prologue(k_eq_v, fraction):
+    case = make_prefill_case(8, 2, 256, 64, [70, 33, 5], seed=2600 + int(k_eq_v),
+                             start_pos=[0, 40, 0], theta=1e4, window=64)
+    kp, vp, table, okp, ovp = _pools_with_prefix(case)
+    D = case.head_dim
+    max_pos = int((case.start_pos + np.diff(case.cu_seqlens)).max()) + 1
+    cos, sin = pkv.rope_table(max_pos, D, case.theta, rotary_fraction=fraction)
+    q_out = torch.full(case.q.shape, -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    v_in = case.k if k_eq_v else case.v
+    pro = dict(q_norm_w=dev_bits(case.q_norm_w), k_norm_w=dev_bits(case.k_norm_w),
+               eps=case.eps, cos=cos, sin=sin, k=dev_bits(case.k), v=dev_bits(v_in),
+               q_out=q_out, v_norm=True)
+    q = dev_bits(case.q)
+    out = pkv.attn_prefill(q, dev_i32(case.cu_seqlens), dev_i32(case.slots), table, kp, vp,
+                           scale=case.scale, window=case.window,
+                           start_pos=dev_i32(case.start_pos), max_seqlen_q_hint=70, prologue=pro)
+    torch.cuda.synchronize()
+    tsl, tpos = case.token_slots(), case.token_pos()
+    q2, k2, v2 = oracle.prologue_gemma4(case.q, case.k, case.v, case.q_norm_w, case.k_norm_w,
+                                        tpos, case.eps, case.theta, rotary_fraction=fraction,
+                                        k_eq_v=k_eq_v)
+    q2b, k2b, v2b = (oracle.f64_to_bf16_bits(x) for x in (q2, k2, v2))
+    oracle.append(okp, ovp, case.table, k2b, v2b, tsl, tpos)
+    # q', k', v' within tolerance of the fp64 values and almost always their nearest bf16
+    gq = host_bits(q_out)
+    assert_attn_close(oracle.bf16_bits_to_f64(gq), q2, "q'")
+    assert np.mean(gq == q2b) >= 0.99
+    for name, g, o in (("k'", host_bits(kp), okp), ("v'", host_bits(vp), ovp)):
+        written = o != 0xFFFF
+        assert np.array_equal(g == 0xFFFF, ~written), f"{name} rows written at the wrong places"
+        d = oracle.bf16_bits_to_f64(g[written]) - oracle.bf16_bits_to_f64(o[written])
+        assert np.max(np.abs(d)) <= 2e-2, name
+        assert np.mean(g[written] == o[written]) >= 0.99, name
+    ref, _ = oracle.attn_prefill(q2b, okp, ovp, case.table, case.cu_seqlens, case.slots,
+                                 case.start_pos, case.scale, case.window)
+    assert_attn_close(host_f64(out), ref, f"gemma4 k_eq_v={k_eq_v} fraction={fraction}")
+
+
 def test_rope_table_matches_fp64():
     D, theta, max_pos = 128, 1e6, 4096
     c, s = pkv.rope_table(max_pos, D, theta)
