@@ -7,8 +7,8 @@ import torch
 import oracle
 import paged_kv_attention_pagetable_amd as pkv
 from synth import CONFIGS, config_lengths, make_decode_case
-from tests.gpu_util import (assert_attn_close, dev_i32, gpu_decode_setup, host_bits, host_f64,
-                            oracle_decode_pools, run_gpu_decode)
+from tests.gpu_util import (DEV, assert_attn_close, dev_bits, dev_i32, gpu_decode_setup,
+                            host_bits, host_f64, oracle_decode_pools, run_gpu_decode)
 
 pytestmark = pytest.mark.gpu
 
@@ -181,3 +181,71 @@ def test_full_gemma_sliding_and_full_layers_sampled():
     _sampled_check(case, hint)
     case, hint = _full_case("gemma_mixed", layer_dim=c["full_dim"])
     _sampled_check(case, hint)
+
+
+def test_decode_graph_replays_track_new_inputs():
+    """One decode call (fused append) captured in a HIP graph and replayed with
+    new q, new-token K/V and shorter lengths written into its static inputs
+    between replays: every replay equals the eager call on the same inputs
+    bit for bit and matches the oracle.  (Replays reuse the library's split
+    arrival counters and the workspace; the path records no memset nodes.)"""
+    case = make_decode_case(32, 8, 128, 128, [900, 300, 0, 2049, 77], max_slots=7, seed=1700,
+                            spare_pages=2)
+    kp, vp, table = gpu_decode_setup(case, with_new_token=False)
+    hint = 2049
+    ws = pkv.new_decode_workspace(pkv.decode_workspace_size(case.B, 32, 8, 128, hint), "cuda")
+    q_s = dev_bits(case.q)
+    kn_s, vn_s = dev_bits(case.k_new), dev_bits(case.v_new)
+    slots_s, lens_s = dev_i32(case.slots), dev_i32(case.seq_lens)
+    out_s = torch.empty_like(q_s)
+    lse_s = torch.empty((case.B, 32), dtype=torch.float32, device=DEV)
+
+    def call(out, lse):
+        pkv.attn_decode(q_s, slots_s, lens_s, table, kp, vp, scale=case.scale,
+                        max_seq_len_hint=hint, k_new=kn_s, v_new=vn_s, out=out, lse=lse,
+                        workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out_s, lse_s)                       # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out_s, lse_s)
+
+    okp, ovp = case.empty_pools()
+    hk, hv, hs, hp = case.history_tokens()
+    oracle.append(okp, ovp, case.table, hk, hv, hs, hp)
+    rng = np.random.default_rng(5)
+    lens = case.seq_lens.copy()
+    for r in range(3):
+        if r:  # new inputs: fresh q and new token, one key fewer for the active rows
+            lens = np.where(lens > 1, lens - 1, lens)
+        q_r = case.q if r == 0 else \
+            oracle.f64_to_bf16_bits(rng.standard_normal(case.q.shape))
+        kn_r = case.k_new if r == 0 else \
+            oracle.f64_to_bf16_bits(rng.standard_normal(case.k_new.shape))
+        vn_r = case.v_new if r == 0 else \
+            oracle.f64_to_bf16_bits(rng.standard_normal(case.v_new.shape))
+        q_s.copy_(dev_bits(q_r))
+        kn_s.copy_(dev_bits(kn_r))
+        vn_s.copy_(dev_bits(vn_r))
+        lens_s.copy_(dev_i32(lens))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got, got_lse = out_s.clone(), lse_s.clone()
+        # the oracle: this replay's new token lands at position len-1 of each active row
+        act = (case.slots != 0) & (lens > 0)
+        oracle.append(okp, ovp, case.table, kn_r[act], vn_r[act], case.slots[act], lens[act] - 1)
+        ref, _ = oracle.attn_decode(q_r, okp, ovp, case.table, case.slots, lens, case.scale, 0)
+        assert_attn_close(host_f64(got), ref, f"replay {r}")
+        # eager call on the same (now already appended) inputs: identical bits
+        e_out, e_lse = torch.empty_like(out_s), torch.empty_like(lse_s)
+        call(e_out, e_lse)
+        torch.cuda.synchronize()
+        assert torch.equal(e_out.view(torch.int16), got.view(torch.int16)), f"replay {r} vs eager"
+        assert torch.equal(e_lse, got_lse)
+    assert np.array_equal(host_bits(kp), okp) and np.array_equal(host_bits(vp), ovp)
