@@ -5,10 +5,13 @@
 // dimension (column = token * G + head), so each K/V tile serves all of them.
 // A workgroup is 4 wave64s, each owning NT 16-column tiles (32 query columns
 // per wave at head_dim <= 128).  Registers are capped so that two waves run
-// per SIMD (two workgroups per CU): one wave's softmax overlaps the other's
-// MFMAs.  (64 columns per wave halve the LDS operand traffic but need ~350
-// registers, one wave per SIMD, and then the softmax serialises with the
-// MFMAs -- measured slower.)
+// per SIMD (two independent workgroups per CU), each filling the other's
+// latency gaps.  (64 columns per wave halve the LDS operand traffic but need
+// ~350 registers and one wave per SIMD; 8-wave workgroups put two waves of
+// one item on each SIMD, in lockstep or in an explicit MFMA / softmax
+// ping-pong -- all measured slower.)
+// With the fused prologue, q is normalised and rotated in registers as an
+// item loads it (norm_rope_q).
 //
 // Keys advance in 64-key chunks.  Each chunk's K rows and V^T rows are copied
 // from their physical pages straight into LDS with gfx950's global-to-LDS
