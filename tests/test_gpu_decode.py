@@ -24,6 +24,7 @@ CASES = {
     "g1": (8, 8, 128, 128, [500, 1], 0, None),
     "g16": (16, 1, 64, 32, [200, 33], 0, None),
     "w1": (4, 2, 64, 16, [37, 50], 1, None),
+    "d128_ps256": (16, 4, 128, 256, [700, 255, 256, 257, 1, 0, 2000], 0, None),
 }
 
 
