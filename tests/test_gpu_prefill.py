@@ -25,6 +25,9 @@ CASES = {
     "slot0_pad": (8, 2, 64, 16, [20, 12, 30], None, 0),
     "ps256_prefix": (16, 4, 128, 256, [300, 520, 17], [0, 250, 0], 0),
     "d64_w100_prefix": (8, 2, 64, 64, [150, 64], [30, 0], 100),
+    # empty prompts first, between and last (repeated cu_seqlens entries);
+    # the empty ones with a cached prefix still own pages and read nothing
+    "empty_prompts": (32, 8, 128, 64, [0, 70, 0, 0, 33, 0], [0, 0, 40, 0, 10, 64], 0),
 }
 
 
@@ -180,7 +183,7 @@ def _check_with_prologue(case, kp, vp, table, okp, ovp, name, hint=None):
 
 
 @pytest.mark.parametrize("name", ["tiny", "d128_g4_ragged", "d128_g4_prefix", "d256_w64",
-                                  "slot0_pad"])
+                                  "slot0_pad", "empty_prompts"])
 def test_prefill_with_prologue_matches_oracle(name):
     case = _case(name, seed=7)
     kp, vp, table, okp, ovp = _pools_with_prefix(case)
