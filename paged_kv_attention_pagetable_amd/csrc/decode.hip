@@ -471,6 +471,9 @@ void decode_keysplit_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // head_dim >= 256: the 4 waves split head_dim; all walk the same chunks.
+// Each wave copies the K slice of its dims (32 rows of DW bf16: whole cache
+// lines) into its own LDS stage by global-to-LDS copies, like the key-split
+// kernel on long splits; the stages become the output buffer at the end.
 // At least three waves per SIMD (head_dim 512 would otherwise take 187
 // registers and two): more workgroups per CU hide the per-chunk barrier and
 // keep more bytes in flight (measured 5 % faster on the Gemma shapes; a
@@ -479,9 +482,14 @@ template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void decode_dimsplit_kernel(DecodeArgs a) {
   constexpr int DW = D / kDecodeWaves;  // dims per wave
+  constexpr int kStage = 32 * DW * 2;   // bytes of a wave's K stage
+  static_assert(kDecodeWaves * kStage >= kMaxGD * (int)sizeof(float), "s_o must fit the stages");
   __shared__ int s_pg[kSegPages];
   __shared__ f32x4 s_part[2][kDecodeWaves][2][64];  // [buffer][wave][rg][lane]
-  __shared__ float s_o[kMaxGD];                     // [G][D] final unnormalised output
+  // the waves' K stages during the key loop, then s_o = [G][D] final
+  // unnormalised output (the loop's last barrier orders the reuse)
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[kDecodeWaves * kStage];
+  float* const s_o = reinterpret_cast<float*>(s_stage);
   __shared__ float s_ml[32];
   const int hk = blockIdx.x, b = blockIdx.y, s = a.max_splits - 1 - (int)blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -526,17 +534,31 @@ void decode_dimsplit_kernel(DecodeArgs a) {
         qreg[c] = qc < G ? v : u32x4{0, 0, 0, 0};
       }
     }
+    uint8_t* kst = s_stage + w * kStage;
     for (int t0 = seg0; t0 < seg1; t0 += 32, ++it) {
-      u32x4 kop[2][DW / 32];
+      // K slice: copy i, lane l fills stage bytes 1024*i + 16*l = row r, slot
+      // u from the wave's dims unit u ^ kst_swz(r) of key t0 + r.  Keys >=
+      // seg1 read a row of page 0 or of the chunk's own page (in the pool);
+      // their scores are masked.
+      if (ps >= 32) {
+        const int pg = __builtin_amdgcn_readfirstlane(max(s_pg[(t0 >> log2ps) - p0], 0));
+        const bf16_t* ks = kbase + (size_t)pg * page_stride + (size_t)(t0 & (ps - 1)) * D;
 #pragma unroll
-      for (int rg = 0; rg < 2; ++rg) {
-        const int tk = t0 + 8 * (qc >> 2) + 4 * rg + (qc & 3);
-        const int page = tk < seg1 ? s_pg[(tk >> log2ps) - p0] : -1;
-        const bf16_t* kp = kbase + (size_t)max(page, 0) * page_stride + (size_t)(tk & (ps - 1)) * D + 8 * quad;
+        for (int i = 0; i < kStage / 1024; ++i) {
+          const int o = 1024 * i + 16 * lane;
+          const int rr = o / (2 * DW), u = ((o % (2 * DW)) >> 4) ^ kst_swz<DW>(o / (2 * DW));
+          __builtin_amdgcn_global_load_lds(ks + rr * D + 8 * u, (lds_void_ptr)(kst + 1024 * i), 16, 0, kNtAux);
+        }
+      } else {
 #pragma unroll
-        for (int c = 0; c < DW / 32; ++c) {
-          const u32x4 v = load16(kp + 32 * c);  // unconditional: the wait counts stay exact
-          kop[rg][c] = page >= 0 ? v : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < kStage / 1024; ++i) {
+          const int o = 1024 * i + 16 * lane;
+          const int rr = o / (2 * DW), u = ((o % (2 * DW)) >> 4) ^ kst_swz<DW>(o / (2 * DW));
+          const int tk = t0 + rr;
+          const int pg = s_pg[min((tk >> log2ps) - p0, kSegPages - 1)];
+          const int page = tk < seg1 ? max(pg, 0) : 0;
+          __builtin_amdgcn_global_load_lds(kbase + (size_t)page * page_stride + (size_t)(tk & (ps - 1)) * D + 8 * u,
+                                           (lds_void_ptr)(kst + 1024 * i), 16, 0, kNtAux);
         }
       }
       const int tv = t0 + 8 * quad;
@@ -548,14 +570,20 @@ void decode_dimsplit_kernel(DecodeArgs a) {
       u32x4 vop[DW / 16];
 #pragma unroll
       for (int dt = 0; dt < DW / 16; ++dt) {
-        const u32x4 v = load16(vp + ((size_t)16 * dt << lgv));
+        const u32x4 v = load16_nt(vp + ((size_t)16 * dt << lgv));
         vop[dt] = vpage >= 0 ? (nvalid < 8 ? keep_first(v, nvalid) : v) : u32x4{0, 0, 0, 0};
       }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the K copies have landed in the stage
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);  // (and the stage reads stay after it)
 #pragma unroll
       for (int rg = 0; rg < 2; ++rg) {
+        const int rr = 8 * (qc >> 2) + 4 * rg + (qc & 3);
         f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < DW / 32; ++c) sacc = mfma16x16x32(kop[rg][c], qreg[c], sacc);
+        for (int c = 0; c < DW / 32; ++c) {
+          const u32x4 kv = *reinterpret_cast<const u32x4*>(kst + rr * (2 * DW) + 16 * ((4 * c + quad) ^ kst_swz<DW>(rr)));
+          sacc = mfma16x16x32(kv, qreg[c], sacc);
+        }
         s_part[it & 1][w][rg][lane] = sacc;
       }
       __syncthreads();
@@ -573,7 +601,7 @@ void decode_dimsplit_kernel(DecodeArgs a) {
       for (int j = 0; j < 8; ++j) {
         const int tk = tv + j;
         const float v = (j < 4 ? S[0][j] : S[1][j - 4]) * a.scale_log2;
-        sc[j] = (tk >= r.lo && tk < seg1) ? v : -INFINITY;
+        sc[j] = (tk >= r.lo && tk < seg1 && vpage >= 0) ? v : -INFINITY;
         mx = fmaxf(mx, sc[j]);
       }
       mx = fmaxf(mx, shfl_xor(mx, 16));
