@@ -16,6 +16,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - bf16 tensors are passed as `void*` to 16-bit storage (IEEE bfloat16).
+ *   The kernels move rows in 16-byte units: every bf16 buffer argument (and
+ *   the fp32 rotary tables) must be 16-byte aligned, else the call returns
+ *   PKV_ERR_INVALID_ARG.
  * - "device" pointers must be device memory of the current HIP device (or
  *   memory the device can read/write); "host" pointers are plain host memory.
  * - Ownership: the caller owns every buffer.  Compute entry points never

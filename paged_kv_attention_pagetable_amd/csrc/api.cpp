@@ -1,5 +1,6 @@
 // C-ABI entry points: host-side argument checks, then kernel launches.
 // Nothing here allocates, frees or synchronises device memory.
+#include <initializer_list>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -15,6 +16,13 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// The kernels move bf16 rows and fp32 table rows in 16-byte units.
+bool misaligned16(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (p && (reinterpret_cast<uintptr_t>(p) & 15u)) return true;
+  return false;
+}
 
 pkv_status fail(pkv_status st, const char* fmt, ...) {
   char buf[512];
@@ -137,6 +145,8 @@ pkv_status pkv_append(const void* k_new, const void* v_new, const int32_t* slot,
   if (T == 0) return PKV_OK;
   if (!k_new || !v_new || !slot || !pos || !k_pool || !v_pool)
     return fail(PKV_ERR_INVALID_ARG, "%s: NULL tensor pointer", fn);
+  if (misaligned16({k_new, v_new, k_pool, v_pool}))
+    return fail(PKV_ERR_INVALID_ARG, "%s: bf16 buffers must be 16-byte aligned", fn);
   pkv::AppendArgs a;
   a.k_new = static_cast<const pkv::bf16_t*>(k_new);
   a.v_new = static_cast<const pkv::bf16_t*>(v_new);
@@ -195,6 +205,8 @@ pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slot
     return fail(PKV_ERR_INVALID_ARG, "%s: NULL tensor pointer", fn);
   if ((k_new == nullptr) != (v_new == nullptr))
     return fail(PKV_ERR_INVALID_ARG, "%s: k_new and v_new must both be given or both be NULL", fn);
+  if (misaligned16({q, k_pool, v_pool, out, k_new, v_new}))
+    return fail(PKV_ERR_INVALID_ARG, "%s: bf16 buffers must be 16-byte aligned", fn);
   const pkv::DecodePlan plan =
       pkv::plan_decode(B, n_q_heads, g.n_kv, g.head_dim, max_seq_len_hint, window);
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
@@ -265,6 +277,10 @@ pkv_status pkv_attn_prefill(const void* q, int32_t n_q_heads, const int32_t* cu_
   if (n_seqs == 0 || total_tokens == 0) return PKV_OK;
   if (!q || !cu_seqlens || !slots || !k_pool || !v_pool || !out)
     return fail(PKV_ERR_INVALID_ARG, "%s: NULL tensor pointer", fn);
+  if (misaligned16({q, k_pool, v_pool, out}) ||
+      (pro && misaligned16({pro->q_norm_w, pro->k_norm_w, pro->rope_cos, pro->rope_sin, pro->k_raw,
+                            pro->v_raw, pro->q_out})))
+    return fail(PKV_ERR_INVALID_ARG, "%s: bf16 buffers and rotary tables must be 16-byte aligned", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (validation_on()) {
     st = launched(pkv::launch_validate_rows(tr, g, slots, nullptr, cu_seqlens, start_pos, n_seqs, s), fn);

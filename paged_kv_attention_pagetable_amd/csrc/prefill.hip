@@ -65,12 +65,20 @@ constexpr int dma_per_wave() { return D / (8 * prefill_waves<D>()); }  // 1 KB c
 // Swizzles (16-byte slot of a row).  K row r holds chunk c (dims 8c..8c+7) at
 // slot c ^ k_swz(r); V^T row d holds key group g (keys 8g..8g+7) at slot
 // g ^ v_swz(d).  Both are bijections within a row; for the 16 rows one MFMA
-// operand read touches they give 16 distinct 16-byte bank groups.
+// operand read touches (K: 16 consecutive rows; V^T: the rows vrow(dt, 0..15)
+// below) they give 16 distinct 16-byte bank groups.
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
   return D == 64 ? (((r >> 1) + 2 * (r >> 4)) & 7) : ((r + 4 * (r >> 4)) & 15);
 }
-__device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
+__device__ __forceinline__ int v_swz(int d) { return ((d >> 1) & 1) | (((d >> 3) & 3) << 1); }
+
+// The P.V MFMA dt takes as its A row m the V^T row (head_dim index)
+//   vrow(dt, m) = 8*(m/4) + m%4 + 32*(dt/2) + 4*(dt%2),
+// so the accumulator lane (column, quad) of MFMAs 2k and 2k+1 holds dims
+// 32k + 8*quad .. +7 of its column: one 16-byte store each (a bijection of
+// the head_dim rows; the swizzle above is the same for all dt).
+__device__ __forceinline__ int vrow_step(int dt) { return 32 * (dt >> 1) + 4 * (dt & 1); }
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
@@ -102,8 +110,9 @@ template <int D>
 struct LaneConst {
   // LDS byte offsets (within a tile buffer) of this lane's MFMA operand rows.
   // K row r, dims chunk c sits at kofs ^ (64 * c): the row's swizzle is folded
-  // into kofs and 64*c only flips bits inside the row.  V^T rows d = 16*dt + qc
-  // share one swizzle across dt, so dt is a plain 2 KB step from vofs.
+  // into kofs and 64*c only flips bits inside the row.  V^T rows vrow(dt, qc)
+  // share one swizzle across dt, so dt is a plain vrow_step(dt) * 128 byte
+  // step from vofs.
   int kofs[2][2], vofs[2];
 };
 
@@ -138,7 +147,8 @@ __device__ __forceinline__ void lane_const(LaneConst<D>& lc, int lane, int w, in
       const int r = 32 * h + 8 * (qc >> 2) + 4 * rg + (qc & 3);
       lc.kofs[h][rg] = r * (2 * D) + 16 * (quad ^ k_swz<D>(r));
     }
-    lc.vofs[h] = k_tile_bytes<D>() + qc * 128 + 16 * ((4 * h + quad) ^ v_swz(qc));
+    const int d0 = 8 * (qc >> 2) + (qc & 3);  // vrow(0, qc)
+    lc.vofs[h] = k_tile_bytes<D>() + d0 * 128 + 16 * ((4 * h + quad) ^ v_swz(d0));
   }
   (void)w;
   (void)ps;
@@ -442,7 +452,7 @@ __device__ __forceinline__ bool zero_tail(uint8_t* lds, int buf, int j0, int kv_
 // Online-softmax state of a wave's NT column tiles.
 template <int D, int NT>
 struct SoftmaxAcc {
-  f32x4 o[NT][D / 16];  // O^T accumulators: lane rows d = 16*dt + 4*(lane/16) + r, column lane%16
+  f32x4 o[NT][D / 16];  // O^T accumulators: lane rows d = vrow(dt, 4*(lane/16) + r), column lane%16
   float m_run[NT];      // reference max (log2 units)
   float neg_m[NT];      // -m_run (0 while m_run = -inf)
   float thr[NT];        // raw-score threshold (m_run + 8) / c above which m_run must move
@@ -545,10 +555,10 @@ __device__ __forceinline__ void chunk_math(const PrefillArgs& a, const uint8_t* 
       // log-sum-exp up to 2^-9 of relative accuracy)
       sa.l_run[nt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     }
-    // ---- O^T += V^T P^T for this half; lane row d = 16*dt + qc, keys group 4h + quad
+    // ---- O^T += V^T P^T for this half; lane A row = V^T row vrow(dt, qc), keys group 4h + quad
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const u32x4 vv = *reinterpret_cast<const u32x4*>(lds + buf_off + lc.vofs[h] + dt * 2048);
+      const u32x4 vv = *reinterpret_cast<const u32x4*>(lds + buf_off + lc.vofs[h] + vrow_step(dt) * 128);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) sa.o[nt][dt] = mfma16x16x32(vv, pb[nt], sa.o[nt][dt]);
     }
@@ -571,12 +581,11 @@ __device__ __forceinline__ void store_out(const PrefillArgs& a, const Item& it, 
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     bf16_t* orow = a.out + ((size_t)(it.a0 + it.i0 + i) * a.n_q + it.hk * G + g) * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const f32x4 o = sa.o[nt][dt];
-      uint2 pk2;
-      pk2.x = pack_bf16x2(o[0] * inv, o[1] * inv);
-      pk2.y = pack_bf16x2(o[2] * inv, o[3] * inv);
-      *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * quad) = pk2;
+    for (int k = 0; k < D / 32; ++k) {  // dims 32k + 8*quad .. +7 (see vrow)
+      const f32x4 o0 = sa.o[nt][2 * k], o1 = sa.o[nt][2 * k + 1];
+      store16(orow + 32 * k + 8 * quad,
+              u32x4{pack_bf16x2(o0[0] * inv, o0[1] * inv), pack_bf16x2(o0[2] * inv, o0[3] * inv),
+                    pack_bf16x2(o1[0] * inv, o1[1] * inv), pack_bf16x2(o1[2] * inv, o1[3] * inv)});
     }
     if (a.lse && quad == 0)
       a.lse[(size_t)(it.a0 + it.i0 + i) * a.n_q + it.hk * G + g] =

@@ -37,9 +37,12 @@ def _pt(table=1, max_slots=3, pps=4):
     return _lib.PageTableRef(table, max_slots, pps)
 
 
+P = 256   # a fake, 16-byte aligned device address: every call below returns before a launch
+
+
 def _decode(**kw):
-    args = dict(q=1, n_q=4, slots=1, seq_lens=1, B=2, hint=64, pt=_pt(), cd=_desc(), k=1, v=1,
-                scale=0.125, window=0, out=1, lse=None, ws=None, ws_bytes=0)
+    args = dict(q=P, n_q=4, slots=P, seq_lens=P, B=2, hint=64, pt=_pt(), cd=_desc(), k=P, v=P,
+                scale=0.125, window=0, out=P, lse=None, ws=None, ws_bytes=0)
     args.update(kw)
     a = args
     return pkv.lib().pkv_attn_decode(a["q"], a["n_q"], a["slots"], a["seq_lens"], a["B"],
@@ -61,7 +64,11 @@ def test_decode_argument_checks_return_before_launch():
     assert _decode(scale=float("nan")) == 1
     assert _decode(hint=0) == 1
     assert _decode(B=-1) == 1
-    assert _decode(k_new=1) == 1                     # k_new without v_new
+    assert _decode(k_new=P) == 1                     # k_new without v_new
+    assert _decode(q=P + 8) == 1                     # bf16 buffers must be 16-byte aligned
+    assert b"aligned" in pkv.lib().pkv_last_error()
+    assert _decode(out=P + 2) == 1
+    assert _decode(k_new=P + 4, v_new=P) == 1
     assert _decode(n_q=2 * 16, cd=_desc(D=256)) == 2  # G * head_dim above 2048
     # a split-K plan needs a workspace
     need = pkv.decode_workspace_size(64, 32, 8, 128, 4096, 0)
@@ -83,26 +90,30 @@ def test_workspace_size_plan_is_monotone_and_zero_when_unsplit():
 def test_append_and_prefill_argument_checks():
     L = pkv.lib()
     cd = _desc()
-    assert L.pkv_append(1, 1, 1, 1, -1, _pt(), ctypes.byref(cd), 1, 1, None) == 1
-    assert L.pkv_append(1, 1, 1, 1, 0, _pt(), ctypes.byref(cd), 1, 1, None) == 0  # T = 0 no-op
-    assert L.pkv_append(None, 1, 1, 1, 5, _pt(), ctypes.byref(cd), 1, 1, None) == 1
+    assert L.pkv_append(P, P, P, P, -1, _pt(), ctypes.byref(cd), P, P, None) == 1
+    assert L.pkv_append(P, P, P, P, 0, _pt(), ctypes.byref(cd), P, P, None) == 0  # T = 0 no-op
+    assert L.pkv_append(None, P, P, P, 5, _pt(), ctypes.byref(cd), P, P, None) == 1
+    assert L.pkv_append(P, P, P, P, 5, _pt(), ctypes.byref(cd), P + 2, P, None) == 1  # misaligned pool
     cd512 = _desc(D=512)
-    assert L.pkv_attn_prefill(1, 4, 1, 1, None, 1, 8, 8, _pt(), ctypes.byref(cd512), 1, 1,
-                              0.1, 0, None, 1, None, None, 0, None) == 2
-    assert L.pkv_attn_prefill(None, 4, 1, 1, None, 1, 8, 8, _pt(), ctypes.byref(cd), 1, 1,
-                              0.1, 0, None, 1, None, None, 0, None) == 1
-    bad = _lib.Prologue(None, 1, 1e-6, 1, 1, 16, 1, 1)
-    assert L.pkv_attn_prefill(1, 4, 1, 1, None, 1, 8, 8, _pt(), ctypes.byref(cd), 1, 1, 0.1, 0,
-                              ctypes.byref(bad), 1, None, None, 0, None) == 1
+    assert L.pkv_attn_prefill(P, 4, P, P, None, 1, 8, 8, _pt(), ctypes.byref(cd512), P, P,
+                              0.1, 0, None, P, None, None, 0, None) == 2
+    assert L.pkv_attn_prefill(None, 4, P, P, None, 1, 8, 8, _pt(), ctypes.byref(cd), P, P,
+                              0.1, 0, None, P, None, None, 0, None) == 1
+    bad = _lib.Prologue(None, P, 1e-6, P, P, 16, P, P)
+    assert L.pkv_attn_prefill(P, 4, P, P, None, 1, 8, 8, _pt(), ctypes.byref(cd), P, P, 0.1, 0,
+                              ctypes.byref(bad), P, None, None, 0, None) == 1
     # the prologue's grid covers at most 65535 blocks of 32 tokens
-    good = _lib.Prologue(1, 1, 1e-6, 1, 1, 16, 1, 1)
-    assert L.pkv_attn_prefill(1, 4, 1, 1, None, 1, 2097121, 8, _pt(), ctypes.byref(cd), 1, 1,
-                              0.1, 0, ctypes.byref(good), 1, None, None, 0, None) == 2
+    good = _lib.Prologue(P, P, 1e-6, P, P, 16, P, P)
+    skew = _lib.Prologue(P, P, 1e-6, P + 4, P, 16, P, P)   # misaligned cos table
+    assert L.pkv_attn_prefill(P, 4, P, P, None, 1, 8, 8, _pt(), ctypes.byref(cd), P, P,
+                              0.1, 0, ctypes.byref(skew), P, None, None, 0, None) == 1
+    assert L.pkv_attn_prefill(P, 4, P, P, None, 1, 2097121, 8, _pt(), ctypes.byref(cd), P, P,
+                              0.1, 0, ctypes.byref(good), P, None, None, 0, None) == 2
     # prefill scale must be > 0
-    assert L.pkv_attn_prefill(1, 4, 1, 1, None, 1, 8, 8, _pt(), ctypes.byref(cd), 1, 1,
-                              -0.1, 0, None, 1, None, None, 0, None) == 1
-    assert L.pkv_attn_prefill(1, 4, 1, 1, None, 1, 8, 8, _pt(), ctypes.byref(cd), 1, 1,
-                              0.0, 0, None, 1, None, None, 0, None) == 1
+    assert L.pkv_attn_prefill(P, 4, P, P, None, 1, 8, 8, _pt(), ctypes.byref(cd), P, P,
+                              -0.1, 0, None, P, None, None, 0, None) == 1
+    assert L.pkv_attn_prefill(P, 4, P, P, None, 1, 8, 8, _pt(), ctypes.byref(cd), P, P,
+                              0.0, 0, None, P, None, None, 0, None) == 1
     assert L.pkv_rope_table(None, 1, 8, 64, 1e6, None) == 1
     # the prefill kernels need no workspace; validation-flag reads need an output
     assert L.pkv_prefill_workspace_size(4096, 16, 32) == 0
