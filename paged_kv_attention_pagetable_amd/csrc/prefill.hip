@@ -82,6 +82,17 @@ __device__ __forceinline__ int vrow_step(int dt) { return 32 * (dt >> 1) + 4 * (
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// accesses, not for its global loads and stores in flight (__syncthreads()
+// drains those too).  The signal fences keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // Max of the 8 scores a lane holds for its column (two 4-row accumulators).
@@ -165,13 +176,33 @@ struct Item {
   const int32_t* trow;
 };
 
-__device__ __forceinline__ void item_init(const PrefillArgs& a, int hk, int n, int qb, Item& it) {
+// A sequence's metadata, the same for all of a workgroup's items.
+struct SeqMeta {
+  int a0, len, sp, slot;
+};
+
+// Loaded once per workgroup, all four loads in flight together (start_pos,
+// when absent, re-reads cu_seqlens[n] and is replaced by 0).
+__device__ __forceinline__ SeqMeta seq_meta(const PrefillArgs& a, int n) {
+  SeqMeta m;
+  const int c0 = a.cu_seqlens[n], c1 = a.cu_seqlens[n + 1];
+  const int spv = (a.start_pos ? a.start_pos : a.cu_seqlens)[n];
+  const int slot = a.slots[n];
+  m.a0 = __builtin_amdgcn_readfirstlane(c0);
+  m.len = __builtin_amdgcn_readfirstlane(c1 - c0);
+  m.sp = a.start_pos ? __builtin_amdgcn_readfirstlane(spv) : 0;
+  m.slot = __builtin_amdgcn_readfirstlane(slot);
+  return m;
+}
+
+__device__ __forceinline__ void item_init(const PrefillArgs& a, const SeqMeta& sm, int hk, int n,
+                                          int qb, Item& it) {
   it.hk = hk;
   it.n = n;
-  it.a0 = a.cu_seqlens[n];
-  const int len = a.cu_seqlens[n + 1] - it.a0;
-  it.sp = a.start_pos ? a.start_pos[n] : 0;
-  const int slot = a.slots[n];
+  it.a0 = sm.a0;
+  const int len = sm.len;
+  it.sp = sm.sp;
+  const int slot = sm.slot;
   it.idle = slot <= 0 || slot >= a.pt.max_slots || it.sp < 0;
   it.i0 = qb * a.q_tokens;
   it.nq = min(a.q_tokens, len - it.i0);
@@ -201,12 +232,6 @@ __device__ __forceinline__ Item load_item(const Item* p) {
 // -1 (read as page 0, whose keys are masked or zeroed).
 __device__ __forceinline__ int checked_page(int pg, int n_pages) {
   return (pg >= 1 && pg < n_pages) ? pg : -1;
-}
-
-// Stage the item's page ids into s_pg (callers place the barriers).
-template <int D>
-__device__ __forceinline__ void stage_pages(const Item& it, int* s_pg, int tid, int n_pages) {
-  for (int i = tid; i < it.n_pg; i += prefill_threads<D>()) s_pg[i] = checked_page(it.trow[it.pg0 + i], n_pages);
 }
 
 // ---------------------------------------------------------------------------
@@ -348,10 +373,7 @@ __device__ __forceinline__ void load_q(const PrefillArgs& a, const Item& it, int
     const bf16_t* qrow = a.q + qoff;
     wq.qout_row[nt] = a.q_out + qoff;  // (only dereferenced when q_out is given)
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      const u32x4 v = load16(qrow + 32 * c);
-      wq.q[nt][c] = valid ? v : u32x4{0, 0, 0, 0};
-    }
+    for (int c = 0; c < D / 32; ++c) wq.q[nt][c] = load16(qrow + 32 * c);  // (zeroed by mask_q)
   }
   wq.lo = 0x7fffffff;
   wq.hi = -1;
@@ -361,6 +383,18 @@ __device__ __forceinline__ void load_q(const PrefillArgs& a, const Item& it, int
     wq.lo = it.sp + it.i0 + i_lo;
     wq.hi = it.sp + it.i0 + i_hi;
   }
+}
+
+// Zeroes the operand of columns without a query (their loads re-read the
+// block's first token).  Applied after the item's first wait, so that no
+// use of q forces its loads to complete earlier.
+template <int D, int NT>
+__device__ __forceinline__ void mask_q(WaveQ<D, NT>& wq) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+      if (wq.pcol[nt] < 0) wq.q[nt][c] = u32x4{0, 0, 0, 0};
 }
 
 // ---------------------------------------------------------------------------
@@ -599,34 +633,44 @@ __device__ __forceinline__ void store_out(const PrefillArgs& a, const Item& it, 
 // one is computed), normalise and store.
 // RQ: q arrives raw and gets the fused Qwen3 norm + rotation (norm_rope_q).
 template <int D, int NT, bool RQ>
-__device__ __forceinline__ void run_item(const PrefillArgs& a, int hk, int n, int qb, uint8_t* lds,
+__device__ __forceinline__ void run_item(const PrefillArgs& a, const SeqMeta& sm, int hk, int n, int qb,
+                                         uint8_t* lds,
                                          int* s_pg, const LaneConst<D>& lc, int tid, int lane,
                                          int w, float inv_c) {
   const int quad = lane >> 4;
   Item it;
-  item_init(a, hk, n, qb, it);
+  item_init(a, sm, hk, n, qb, it);
+  // The item's first page ids are loaded first, q (and the rotary inputs)
+  // right behind them, so that they take one memory round trip; without the
+  // q transform the page ids are staged as soon as they arrive and the first
+  // key chunk's copies go out while q is still in flight.  The barriers up to
+  // the first chunk's wait are LDS-only, so they do not drain these loads.
+  const int pg_raw = tid < it.n_pg ? it.trow[it.pg0 + tid] : 0;
   WaveQ<D, NT> wq;
   load_q<D, NT>(a, it, w, lane, wq);
-  if constexpr (RQ) {
-    // head_dim <= 128: the rotary inputs are loaded with q, into registers;
-    // head_dim 256 holds twice as many per lane and loads them per chunk
-    // inside the transform, to stay within the register budget
-    if constexpr (D <= 128) {
-      QRope<D, NT> qr;
-      load_rope<D, NT>(a, quad, wq, qr);
-      norm_rope_q<D, NT, true>(a, quad, &qr, wq);
-    } else {
-      norm_rope_q<D, NT, false>(a, quad, nullptr, wq);
-    }
-  }
+  // head_dim <= 128: the rotary inputs are loaded into registers now;
+  // head_dim 256 holds twice as many per lane and loads them inside the
+  // transform, to stay within the register budget
+  QRope<(RQ && D <= 128) ? D : 64, NT> qr;
+  if constexpr (RQ && D <= 128) load_rope<D, NT>(a, quad, wq, qr);
   SoftmaxAcc<D, NT> sa;
   acc_init(sa);
-  __syncthreads();  // the previous item's tiles and page ids are consumed
-  stage_pages<D>(it, s_pg, tid, a.g.n_pages);
-  __syncthreads();
+  if constexpr (RQ) {
+    // transformed before the page ids are staged: the rotary inputs are then
+    // dead before the first chunk's wait (fewer live registers)
+    mask_q<D, NT>(wq);
+    if constexpr (D <= 128) norm_rope_q<D, NT, true>(a, quad, &qr, wq);
+    else norm_rope_q<D, NT, false>(a, quad, nullptr, wq);
+  }
+  lds_barrier();  // the previous item's tiles and page ids are consumed
+  if (tid < it.n_pg) s_pg[tid] = checked_page(pg_raw, a.g.n_pages);
+  for (int i = tid + prefill_threads<D>(); i < it.n_pg; i += prefill_threads<D>())
+    s_pg[i] = checked_page(it.trow[it.pg0 + i], a.g.n_pages);
+  lds_barrier();  // page ids visible
   if (it.n_chunks > 0) issue_tile<D>(a, it, s_pg, lds, 0, it.j_start, lc, lane, w);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): q, the rotary inputs and the first chunk have landed
   __syncthreads();
+  if constexpr (!RQ) mask_q<D, NT>(wq);
   if (it.n_chunks > 0 && zero_tail<D>(lds, 0, it.j_start, it.kv_hi, tid)) __syncthreads();
   for (int ck = 0; ck < it.n_chunks; ++ck) {
     const int j0 = it.j_start + ck * kChunk;
@@ -658,10 +702,10 @@ void prefill_kernel(PrefillArgs a) {
   lane_const<D>(lc, lane, w, a.g.page_size);
   const int hk = blockIdx.x, n = blockIdx.y;
   if (n >= a.n_seqs) return;  // padding row of the grid (odd y extent)
-  const int len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
-  const int nblk = (len + a.q_tokens - 1) / a.q_tokens;
+  const SeqMeta sm = seq_meta(a, n);
+  const int nblk = (sm.len + a.q_tokens - 1) / a.q_tokens;
   for (int qb = a.n_qblocks - 1 - (int)blockIdx.z; qb < nblk; qb += a.n_qblocks)
-    run_item<D, NT, RQ>(a, hk, n, qb, lds, s_pg, lc, tid, lane, w, inv_c);
+    run_item<D, NT, RQ>(a, sm, hk, n, qb, lds, s_pg, lc, tid, lane, w, inv_c);
 }
 
 // ---------------------------------------------------------------------------
