@@ -82,17 +82,6 @@ __device__ __forceinline__ int vrow_step(int dt) { return 32 * (dt >> 1) + 4 * (
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
-// accesses, not for its global loads and stores in flight (__syncthreads()
-// drains those too).  The signal fences keep the compiler from moving memory
-// accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // Max of the 8 scores a lane holds for its column (two 4-row accumulators).
@@ -176,9 +165,11 @@ struct Item {
   const int32_t* trow;
 };
 
-// A sequence's metadata, the same for all of a workgroup's items.
+// A sequence's metadata, the same for all of a workgroup's items; n_pg =
+// the logical pages any of its items reads (their ids are staged in LDS
+// once per workgroup).
 struct SeqMeta {
-  int a0, len, sp, slot;
+  int a0, len, sp, slot, n_pg;
 };
 
 // Loaded once per workgroup, all four loads in flight together (start_pos,
@@ -192,6 +183,9 @@ __device__ __forceinline__ SeqMeta seq_meta(const PrefillArgs& a, int n) {
   m.len = __builtin_amdgcn_readfirstlane(c1 - c0);
   m.sp = a.start_pos ? __builtin_amdgcn_readfirstlane(spv) : 0;
   m.slot = __builtin_amdgcn_readfirstlane(slot);
+  const bool idle = m.slot <= 0 || m.slot >= a.pt.max_slots || m.sp < 0;
+  const int kv_end = idle ? 0 : min(m.sp + m.len, a.pt.pps * a.g.page_size);
+  m.n_pg = (kv_end + a.g.page_size - 1) >> a.g.log2ps;
   return m;
 }
 
@@ -212,8 +206,8 @@ __device__ __forceinline__ void item_init(const PrefillArgs& a, const SeqMeta& s
   const int kv_lo = a.window > 0 ? max(0, it.sp + it.i0 - a.window + 1) : 0;
   it.j_start = kv_lo & ~(kChunk - 1);
   it.n_chunks = it.kv_hi > it.j_start ? (it.kv_hi - it.j_start + kChunk - 1) / kChunk : 0;
-  it.pg0 = it.j_start >> a.g.log2ps;
-  it.n_pg = it.n_chunks ? ((it.kv_hi - 1) >> a.g.log2ps) - it.pg0 + 1 : 0;
+  it.pg0 = 0;          // s_pg holds the sequence's pages from logical page 0
+  it.n_pg = sm.n_pg;
 }
 
 // An item parked in LDS (written by one thread) read back as uniform values.
@@ -640,12 +634,11 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, const SeqMeta& sm
   const int quad = lane >> 4;
   Item it;
   item_init(a, sm, hk, n, qb, it);
-  // The item's first page ids are loaded first, q (and the rotary inputs)
-  // right behind them, so that they take one memory round trip; without the
-  // q transform the page ids are staged as soon as they arrive and the first
-  // key chunk's copies go out while q is still in flight.  The barriers up to
-  // the first chunk's wait are LDS-only, so they do not drain these loads.
-  const int pg_raw = tid < it.n_pg ? it.trow[it.pg0 + tid] : 0;
+  // The first key chunk's copies go out first and q (and the rotary inputs)
+  // right behind them: one memory round trip before the key loop.  (The page
+  // ids were staged for the whole sequence; the previous item's loop ended
+  // with a barrier, so both tile buffers are free.)
+  if (it.n_chunks > 0) issue_tile<D>(a, it, s_pg, lds, 0, it.j_start, lc, lane, w);
   WaveQ<D, NT> wq;
   load_q<D, NT>(a, it, w, lane, wq);
   // head_dim <= 128: the rotary inputs are loaded into registers now;
@@ -655,22 +648,13 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, const SeqMeta& sm
   if constexpr (RQ && D <= 128) load_rope<D, NT>(a, quad, wq, qr);
   SoftmaxAcc<D, NT> sa;
   acc_init(sa);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first chunk, q and the rotary inputs have landed
+  __syncthreads();
+  mask_q<D, NT>(wq);
   if constexpr (RQ) {
-    // transformed before the page ids are staged: the rotary inputs are then
-    // dead before the first chunk's wait (fewer live registers)
-    mask_q<D, NT>(wq);
     if constexpr (D <= 128) norm_rope_q<D, NT, true>(a, quad, &qr, wq);
     else norm_rope_q<D, NT, false>(a, quad, nullptr, wq);
   }
-  lds_barrier();  // the previous item's tiles and page ids are consumed
-  if (tid < it.n_pg) s_pg[tid] = checked_page(pg_raw, a.g.n_pages);
-  for (int i = tid + prefill_threads<D>(); i < it.n_pg; i += prefill_threads<D>())
-    s_pg[i] = checked_page(it.trow[it.pg0 + i], a.g.n_pages);
-  lds_barrier();  // page ids visible
-  if (it.n_chunks > 0) issue_tile<D>(a, it, s_pg, lds, 0, it.j_start, lc, lane, w);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): q, the rotary inputs and the first chunk have landed
-  __syncthreads();
-  if constexpr (!RQ) mask_q<D, NT>(wq);
   if (it.n_chunks > 0 && zero_tail<D>(lds, 0, it.j_start, it.kv_hi, tid)) __syncthreads();
   for (int ck = 0; ck < it.n_chunks; ++ck) {
     const int j0 = it.j_start + ck * kChunk;
@@ -704,6 +688,12 @@ void prefill_kernel(PrefillArgs a) {
   if (n >= a.n_seqs) return;  // padding row of the grid (odd y extent)
   const SeqMeta sm = seq_meta(a, n);
   const int nblk = (sm.len + a.q_tokens - 1) / a.q_tokens;
+  if (nblk <= a.n_qblocks - 1 - (int)blockIdx.z) return;  // no item in this layer
+  {
+    const int32_t* trow = a.pt.table + (size_t)max(sm.slot, 0) * a.pt.pps;
+    for (int i = tid; i < sm.n_pg; i += prefill_threads<D>()) s_pg[i] = checked_page(trow[i], a.g.n_pages);
+    __syncthreads();
+  }
   for (int qb = a.n_qblocks - 1 - (int)blockIdx.z; qb < nblk; qb += a.n_qblocks)
     run_item<D, NT, RQ>(a, sm, hk, n, qb, lds, s_pg, lc, tid, lane, w, inv_c);
 }
