@@ -508,6 +508,10 @@ __device__ __forceinline__ void chunk_math(const PrefillArgs& a, const uint8_t* 
   const bool skip = wq.hi < 0 || j0 > wq.hi || (a.window > 0 && j0 + kChunk - 1 <= wq.lo - a.window);
   if (skip) return;
   const bool full = (j0 + kChunk - 1 <= wq.lo) && (a.window <= 0 || wq.hi - j0 < a.window);
+  // Scheduling hint for the QK^T block: the compiler's MFMA / LDS-read
+  // interleaving strategy 1 (measured 44.8 -> 43.8 us on the Qwen3 prompts;
+  // strategy 0, or the hint on the P.V blocks too, were slower).
+  __builtin_amdgcn_iglp_opt(1);
   // ---- S^T = K Q^T for the chunk's two 32-key halves h: MFMA rg row m holds
   // key j0 + 32h + 8*(m/4) + 4*rg + m%4
   f32x4 S[2][NT][2];
