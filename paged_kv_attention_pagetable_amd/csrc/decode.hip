@@ -310,11 +310,11 @@ void decode_keysplit_kernel(DecodeArgs a) {
     stage_pages(a, trow, p0, ((seg1 - 1) >> log2ps) - p0 + 1, s_pg);
     __syncthreads();
     if (seg0 == r.start) {
+      // Columns qc >= G repeat head G-1: MFMA columns never mix, and those
+      // are never stored.  (Zeroing them here would wait for q before the
+      // first chunk's K/V loads are issued.)
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        const u32x4 v = load16(qrow + 32 * c);
-        qreg[c] = qc < G ? v : u32x4{0, 0, 0, 0};
-      }
+      for (int c = 0; c < D / 32; ++c) qreg[c] = load16(qrow + 32 * c);
     }
     // A wave's chunk = 32 keys at t0.  K (KLDS): 1 KB global-to-LDS copies
     // into the wave's stage (copy i, lane l: stage bytes 1024*i + 16*l = row
@@ -352,16 +352,17 @@ void decode_keysplit_kernel(DecodeArgs a) {
           }
         }
       } else {
+        // Keys past seg1 or on an unmapped page read page 0 (in the pool); no
+        // zeroing: their scores are masked by selection, and a NaN in a K row
+        // reaches only that key's scores.  (A select on the loaded value here
+        // would wait for each load before the rest are issued.)
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg) {
           const int tk = t0 + 8 * (qc >> 2) + 4 * rg + (qc & 3);
           const int page = tk < seg1 ? s_pg[(tk >> log2ps) - p0] : -1;
           const bf16_t* kp = kbase + (size_t)max(page, 0) * page_stride + (size_t)(tk & (ps - 1)) * D + 8 * quad;
 #pragma unroll
-          for (int c = 0; c < D / 32; ++c) {
-            const u32x4 v = load16_nt(kp + 32 * c);  // unconditional: the wait counts stay exact
-            kop[rg][c] = page >= 0 ? v : u32x4{0, 0, 0, 0};
-          }
+          for (int c = 0; c < D / 32; ++c) kop[rg][c] = load16_nt(kp + 32 * c);
         }
       }
       const int tv = t0 + 8 * quad;
@@ -529,10 +530,7 @@ void decode_dimsplit_kernel(DecodeArgs a) {
     __syncthreads();
     if (seg0 == r.start) {
 #pragma unroll
-      for (int c = 0; c < DW / 32; ++c) {
-        const u32x4 v = load16(qrow + 32 * c);
-        qreg[c] = qc < G ? v : u32x4{0, 0, 0, 0};
-      }
+      for (int c = 0; c < DW / 32; ++c) qreg[c] = load16(qrow + 32 * c);  // (qc >= G: head G-1, unused)
     }
     uint8_t* kst = s_stage + w * kStage;
     for (int t0 = seg0; t0 < seg1; t0 += 32, ++it) {
