@@ -187,6 +187,42 @@ __device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>&
     }
     lds_barrier();
   }
+  // k rows with staged metadata: each lane finds its rows' positions itself
+  // and issues their cos / sin loads now, in flight with the page-table loads
+  // below (one memory round trip instead of two).
+  const int f0 = (8 * c) & (D / 2 - 1);
+  int pos_k[PASSES];
+  float cs[PASSES][8], sn[PASSES][8];
+  auto load_cs = [&]() {
+#pragma unroll
+    for (int k = 0; k < PASSES; ++k) {
+      const size_t ro = (size_t)max(pos_k[k], 0) * (D / 2) + f0;
+#pragma unroll
+      for (int j = 0; j < 8; j += 4) {
+        const f32x4 cv = *reinterpret_cast<const f32x4*>(a.cos_t + ro + j);
+        const f32x4 sv = *reinterpret_cast<const f32x4*>(a.sin_t + ro + j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          cs[k][j + e] = cv[e];
+          sn[k][j + e] = sv[e];
+        }
+      }
+    }
+  };
+  if constexpr (KIND == kHeadK && STAGED) {
+#pragma unroll
+    for (int k = 0; k < PASSES; ++k) {
+      const int tt = rsub + k * ROWS;
+      pos_k[k] = -1;
+      if (tt < nt) {
+        const int t = t0 + tt;
+        const int n = seq_of(sm.cu, a.n_seqs, t);
+        const int slot = sm.slot[n], pos = sm.sp[n] + (t - sm.cu[n]);
+        if (slot > 0 && slot < a.pt.max_slots && pos >= 0 && pos < a.max_pos) pos_k[k] = pos;
+      }
+    }
+    load_cs();
+  }
   if (tid < nt) {
     const int t = t0 + tid;
     int n, cu_n, slot, sp;
@@ -245,27 +281,13 @@ __device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>&
     }
     return;
   }
-  int pos_k[PASSES];
+  if constexpr (!STAGED) {
 #pragma unroll
-  for (int k = 0; k < PASSES; ++k) {
-    const int tt = rsub + k * ROWS;
-    pos_k[k] = tt < nt ? sm.pos[tt] : -1;
-  }
-  const int f0 = (8 * c) & (D / 2 - 1);
-  float cs[PASSES][8], sn[PASSES][8];
-#pragma unroll
-  for (int k = 0; k < PASSES; ++k) {
-    const size_t ro = (size_t)max(pos_k[k], 0) * (D / 2) + f0;
-#pragma unroll
-    for (int j = 0; j < 8; j += 4) {
-      const f32x4 cv = *reinterpret_cast<const f32x4*>(a.cos_t + ro + j);
-      const f32x4 sv = *reinterpret_cast<const f32x4*>(a.sin_t + ro + j);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        cs[k][j + e] = cv[e];
-        sn[k][j + e] = sv[e];
-      }
+    for (int k = 0; k < PASSES; ++k) {
+      const int tt = rsub + k * ROWS;
+      pos_k[k] = tt < nt ? sm.pos[tt] : -1;
     }
+    load_cs();
   }
   const bf16_t* w = a.k_w;
 #pragma unroll
