@@ -228,6 +228,60 @@ class PrefillWorkload:
 # timing
 # ----------------------------------------------------------------------------
 
+def reserve_timing(wl, calls=16, reps=8):
+    """Device-side page reservation (pkv_pt_device_reserve) for the decode batch:
+    us per call when every row with a slot takes one new page.  The state comes
+    from the library's host allocator; it is restored before each timed replay of
+    a graph of `calls` reserves (call i grows each row to i more pages)."""
+    import torch
+    pkv, case = wl.pkv, wl.case
+    ps = case.page_size
+    slots = [int(s) for s in case.slots]
+    lens = [int(L) for L in case.seq_lens]
+    pps = -(-max(lens + [1]) // ps) + calls + 1
+    alloc = pkv.PageAllocator(case.B * pps + 2, ps, case.max_slots)
+    got = [alloc.allocate() for _ in range(case.max_slots - 1)]
+    for s, L in zip(slots, lens):
+        if s > 0 and L > 0:
+            alloc.reserve(s, L)
+    st = alloc.to_device(pps)
+    saved = [t.clone() for t in (st.table, st.free_pages, st.free_count, st.capacity)]
+    cap = st.capacity.cpu()
+    d_slots = torch.tensor(slots, dtype=torch.int32, device="cuda")
+    d_lens = [torch.tensor([int(cap[s]) + i * ps + 1 if s > 0 else 0 for s in slots],
+                           dtype=torch.int32, device="cuda") for i in range(calls)]
+
+    def restore():
+        for t, t0 in zip((st.table, st.free_pages, st.free_count, st.capacity), saved):
+            t.copy_(t0)
+
+    def run():
+        for ln in d_lens:
+            st.reserve(d_slots, ln)
+
+    run()
+    restore()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    times = []
+    for _ in range(reps):
+        restore()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / calls * 1e3)
+    assert int(st.status.item()) == 0, "device reserve reported a failure"
+    del got
+    return dict(us_per_call=round(float(np.median(times)), 3), rows=len(slots),
+                pages_per_call=sum(1 for s in slots if s > 0),
+                kernel="device page reserve (pkv_pt_device_reserve, one workgroup)")
+
+
 def capture(fn):
     import torch
     fn()                       # eager warm-up: no allocation happens inside fn
@@ -589,6 +643,7 @@ def main():
         "step_ms_median": round(float(np.median(each)), 4), "step_ms_best": round(min(each), 4),
     }
     del g_step, g_attn
+    result["device_reserve"] = reserve_timing(wl)
     if args.calibrate_copy:
         src = torch.empty(128 * 2**20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)

@@ -328,6 +328,52 @@ int32_t pkv_pt_row(const pkv_pt* pt, int32_t slot, int32_t* pages_out, int32_t m
 int32_t pkv_pt_free_pages(const pkv_pt* pt, int32_t* pages_out, int32_t max_out);
 pkv_status pkv_pt_export(const pkv_pt* pt, int32_t* table_out, int32_t pages_per_slot);
 
+/* ---------------------------------------------------------------------------
+ * Device-side reserve for a batch ([continuous-batching compare]
+ * flex_paged_attention.py, PageTable.reserve), so that a decode step can grow
+ * its slots' pages without a host round trip, e.g. inside a captured HIP
+ * graph.  The state is the host allocator's, rendered into caller-owned
+ * device buffers (pkv_pt_export, pkv_pt_free_pages, pkv_pt_capacity):
+ *   table      int32 [max_slots][pages_per_slot]: the page table the
+ *              attention calls read; granted pages are written into it
+ *   free_pages int32 [n_pages]: the free-page stack, bottom first
+ *   free_count int32 [1]: its length (clamped to [0, n_pages] when read)
+ *   capacity   int32 [max_slots]: tokens reserved per slot (a multiple of
+ *              page_size)
+ *   status     uint32 [1]: PKV_RESERVE_* bits of rows that could not be
+ *              served are OR-ed in; the call never clears it
+ * pkv_pt_device_reserve(dev, slots, seq_lens, B, stream) applies, on
+ * `stream`, what B host calls reserve(slots[b], seq_lens[b]) in row order
+ * would: a row whose slot is outside [1, max_slots) is skipped; otherwise the
+ * slot's capacity grows to >= seq_lens[b] by granting the top k entries of
+ * the free stack, in stack order, as its next logical pages.  A row that needs
+ * more pages than are free (PKV_RESERVE_NO_PAGES), more than its table row
+ * holds (PKV_RESERVE_TOO_LONG), or whose stored capacity is not a multiple of
+ * page_size within the row (PKV_RESERVE_BAD_STATE) changes nothing, and the
+ * rows after it proceed.  The slots of one call must be distinct (as for
+ * decode).  allocate and erase stay on the host.
+ *   slots, seq_lens : device int32 [B]; B == 0 is a no-op
+ * Returns PKV_ERR_INVALID_ARG for NULL pointers or bad sizes (nothing
+ * enqueued), PKV_ERR_LAUNCH if the launch fails.
+ */
+#define PKV_RESERVE_NO_PAGES 1u
+#define PKV_RESERVE_TOO_LONG 2u
+#define PKV_RESERVE_BAD_STATE 4u
+typedef struct {
+  int32_t* table;
+  int32_t* free_pages;
+  int32_t* free_count;
+  int32_t* capacity;
+  uint32_t* status;
+  int32_t max_slots;
+  int32_t pages_per_slot;
+  int32_t page_size;
+  int32_t n_pages;
+} pkv_pt_device;
+
+pkv_status pkv_pt_device_reserve(const pkv_pt_device* dev, const int32_t* slots,
+                                 const int32_t* seq_lens, int32_t B, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,10 @@ from ._lib import CacheDesc, PageTableRef, Prologue, PkvError, check, lib
 
 __all__ = ["append", "attn_decode", "attn_prefill", "decode_workspace_size", "rope_table",
            "set_validation", "validation_flags", "VALIDATE_SLOT", "VALIDATE_PAGE", "VALIDATE_POS",
-           "new_pools", "v_pool_shape", "new_decode_workspace", "PageAllocator", "PkvError", "lib"]
+           "new_pools", "v_pool_shape", "new_decode_workspace", "PageAllocator", "DevicePageState",
+           "RESERVE_NO_PAGES", "RESERVE_TOO_LONG", "RESERVE_BAD_STATE", "PkvError", "lib"]
+
+RESERVE_NO_PAGES, RESERVE_TOO_LONG, RESERVE_BAD_STATE = 1, 2, 4
 
 
 def _ptr(t):
@@ -301,6 +304,17 @@ class PageAllocator:
         lib().pkv_pt_free_pages(self._h, buf, n)
         return list(buf[:n])
 
+    def to_device(self, pages_per_slot, device="cuda"):
+        """This allocator's state as a ``DevicePageState`` for device-side reserves."""
+        free = self.free_pages()
+        fp = torch.zeros(self.n_pages, dtype=torch.int32)
+        fp[:len(free)] = torch.tensor(free, dtype=torch.int32)
+        cap = torch.tensor([self.capacity(s) if s > 0 else 0 for s in range(self.max_slots)],
+                           dtype=torch.int32)
+        return DevicePageState(self.export(pages_per_slot).to(device), fp.to(device),
+                               torch.tensor([len(free)], dtype=torch.int32, device=device),
+                               cap.to(device), self.page_size)
+
     def export(self, pages_per_slot):
         """Device-format table as an int32 CPU tensor ``[max_slots, pages_per_slot]``."""
         t = torch.empty((self.max_slots, pages_per_slot), dtype=torch.int32)
@@ -308,3 +322,30 @@ class PageAllocator:
                                                        ctypes.POINTER(ctypes.c_int32)),
                                   pages_per_slot))
         return t
+
+
+class DevicePageState:
+    """Device buffers of the allocator state used by ``pkv_pt_device_reserve``:
+    ``table`` int32 [max_slots, pages_per_slot], ``free_pages`` int32 [n_pages]
+    (the free stack, bottom first), ``free_count`` int32 [1], ``capacity``
+    int32 [max_slots] and the ``status`` flag word (uint32 [1], as int32)."""
+
+    def __init__(self, table, free_pages, free_count, capacity, page_size):
+        for t, name in ((table, "table"), (free_pages, "free_pages"), (free_count, "free_count"),
+                        (capacity, "capacity")):
+            _i32(t, name)
+        self.table, self.free_pages, self.free_count, self.capacity = (table, free_pages,
+                                                                        free_count, capacity)
+        self.status = torch.zeros(1, dtype=torch.int32, device=table.device)
+        self.page_size = page_size
+        self._c = _lib.PtDevice(table.data_ptr(), free_pages.data_ptr(), free_count.data_ptr(),
+                                capacity.data_ptr(), self.status.data_ptr(), table.shape[0],
+                                table.shape[1], page_size, free_pages.numel())
+
+    def reserve(self, slots, seq_lens, stream=None):
+        """Grow the slots of rows b (in order) to seq_lens[b] tokens on the device
+        (``pkv_pt_device_reserve``); rows that cannot be served set ``status`` bits."""
+        _i32(slots, "slots")
+        _i32(seq_lens, "seq_lens")
+        check(lib().pkv_pt_device_reserve(ctypes.byref(self._c), _ptr(slots), _ptr(seq_lens),
+                                          slots.numel(), _stream(stream, self.table.device)))

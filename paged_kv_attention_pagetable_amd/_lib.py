@@ -44,6 +44,12 @@ class Prologue(ctypes.Structure):
                 ("v_norm", c_int32)]
 
 
+class PtDevice(ctypes.Structure):
+    _fields_ = [("table", c_void_p), ("free_pages", c_void_p), ("free_count", c_void_p),
+                ("capacity", c_void_p), ("status", c_void_p), ("max_slots", c_int32),
+                ("pages_per_slot", c_int32), ("page_size", c_int32), ("n_pages", c_int32)]
+
+
 class PkvError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -84,6 +90,8 @@ _SIGS = {
     "pkv_pt_row": (c_int32, [c_void_p, c_int32, ctypes.POINTER(c_int32), c_int32]),
     "pkv_pt_free_pages": (c_int32, [c_void_p, ctypes.POINTER(c_int32), c_int32]),
     "pkv_pt_export": (c_int32, [c_void_p, ctypes.POINTER(c_int32), c_int32]),
+    "pkv_pt_device_reserve": (c_int32, [ctypes.POINTER(PtDevice), c_void_p, c_void_p, c_int32,
+                                        c_void_p]),
 }
 
 _lib = None

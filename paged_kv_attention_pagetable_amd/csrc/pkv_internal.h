@@ -140,6 +140,22 @@ hipError_t launch_validate_tokens(const TableRef& pt, const PoolGeom& g, const i
                                   const int32_t* pos, int T, hipStream_t st);
 hipError_t read_validate_flags(uint32_t* host_out, int clear, hipStream_t st);
 
+// Device-side batch reserve (see pkv_pt_device_reserve in the public header).
+struct ReserveArgs {
+  int32_t* table;
+  int32_t* free_pages;
+  int32_t* free_count;
+  int32_t* capacity;
+  uint32_t* status;
+  const int32_t* slots;
+  const int32_t* seq_lens;
+  int B, max_slots, pps, page_size, n_pages;
+};
+constexpr uint32_t kReserveNoPages = 1u;
+constexpr uint32_t kReserveTooLong = 2u;
+constexpr uint32_t kReserveBadState = 4u;
+hipError_t launch_reserve(const ReserveArgs& a, hipStream_t st);
+
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t st);

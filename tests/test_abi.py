@@ -215,3 +215,19 @@ def test_allocator_reports_exhaustion_and_bad_slots():
         pt.erase(0)                   # slot 0 is never granted
     with pytest.raises(pkv.PkvError):
         pt.reserve(3, 1)              # out of range
+
+
+def test_device_reserve_argument_checks():
+    L = pkv.lib()
+    ok = _lib.PtDevice(P, P, P, P, P, 9, 8, 128, 100)
+    assert L.pkv_pt_device_reserve(None, P, P, 4, None) == 1
+    assert L.pkv_pt_device_reserve(ctypes.byref(ok), P, P, -1, None) == 1
+    assert L.pkv_pt_device_reserve(ctypes.byref(ok), P, P, 0, None) == 0      # no-op
+    assert L.pkv_pt_device_reserve(ctypes.byref(ok), None, P, 4, None) == 1
+    for bad in (_lib.PtDevice(P, P, P, P, P, 1, 8, 128, 100),    # slot 0 reserved: max_slots >= 2
+                _lib.PtDevice(P, P, P, P, P, 9, 0, 128, 100),
+                _lib.PtDevice(P, P, P, P, P, 9, 8, 0, 100),
+                _lib.PtDevice(P, P, P, P, P, 9, 8, 128, 1),
+                _lib.PtDevice(None, P, P, P, P, 9, 8, 128, 100),
+                _lib.PtDevice(P, P, P, P, None, 9, 8, 128, 100)):
+        assert L.pkv_pt_device_reserve(ctypes.byref(bad), P, P, 4, None) == 1
