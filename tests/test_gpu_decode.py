@@ -287,3 +287,70 @@ def test_decode_graph_replays_track_new_inputs():
         assert torch.equal(e_out.view(torch.int16), got.view(torch.int16)), f"replay {r} vs eager"
         assert torch.equal(e_lse, got_lse)
     assert np.array_equal(host_bits(kp), okp) and np.array_equal(host_bits(vp), ovp)
+
+
+def test_decode_graph_batch_buckets_with_slot0_padding():
+    """Decode steps captured once per batch bucket (1, 2, 4, 8); a batch of n
+    rows runs in the smallest bucket >= n, the rest padded with slot-0 rows.
+    Each replay appends every real row's new token and attends; real rows
+    match the oracle and equal an eager unpadded call on the same inputs bit
+    for bit, padding rows are exactly 0 and write nothing."""
+    n_q, n_kv, D, ps = 32, 8, 128, 128
+    case = make_decode_case(n_q, n_kv, D, ps, [700, 40, 1500, 129, 900, 2000, 3, 64],
+                            max_slots=10, seed=1900, spare_pages=4, pages_per_slot=17)
+    kp, vp, table = gpu_decode_setup(case, with_new_token=False)
+    hint = 17 * ps
+    okp, ovp = case.empty_pools()
+    hk, hv, hs, hp = case.history_tokens()
+    oracle.append(okp, ovp, case.table, hk, hv, hs, hp)
+    lens = case.seq_lens.copy() - 1                 # keys before this test's first token
+    buckets = {}
+    for nb in (1, 2, 4, 8):
+        st = dict(q=torch.zeros((nb, n_q, D), dtype=torch.bfloat16, device=DEV),
+                  kn=torch.zeros((nb, n_kv, D), dtype=torch.bfloat16, device=DEV),
+                  vn=torch.zeros((nb, n_kv, D), dtype=torch.bfloat16, device=DEV),
+                  slots=dev_i32(np.zeros(nb)), lens=dev_i32(np.zeros(nb)),
+                  out=torch.empty((nb, n_q, D), dtype=torch.bfloat16, device=DEV),
+                  ws=pkv.new_decode_workspace(
+                      pkv.decode_workspace_size(nb, n_q, n_kv, D, hint), "cuda"))
+
+        def call(st=st):
+            pkv.attn_decode(st["q"], st["slots"], st["lens"], table, kp, vp, scale=case.scale,
+                            max_seq_len_hint=hint, k_new=st["kn"], v_new=st["vn"],
+                            out=st["out"], workspace=st["ws"])
+
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):      # all-padding inputs: the capture itself writes nothing
+            call()
+        buckets[nb] = (g, st)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(19)
+    for step, n in enumerate([5, 1, 8, 3, 2, 7, 4]):
+        rows = np.sort(rng.choice(case.B, size=n, replace=False))
+        nb = min(b for b in buckets if b >= n)
+        g, st = buckets[nb]
+        lens[rows] += 1
+        q_r = oracle.f64_to_bf16_bits(rng.standard_normal((n, n_q, D)))
+        kn_r = oracle.f64_to_bf16_bits(rng.standard_normal((n, n_kv, D)))
+        vn_r = oracle.f64_to_bf16_bits(rng.standard_normal((n, n_kv, D)))
+        pad = nb - n
+        st["q"].copy_(dev_bits(np.concatenate([q_r, np.full((pad, n_q, D), 0x3F80, np.uint16)])))
+        st["kn"].copy_(dev_bits(np.concatenate([kn_r, np.full((pad, n_kv, D), 0x3F80, np.uint16)])))
+        st["vn"].copy_(dev_bits(np.concatenate([vn_r, np.full((pad, n_kv, D), 0x3F80, np.uint16)])))
+        st["slots"].copy_(dev_i32(np.concatenate([case.slots[rows], np.zeros(pad)])))
+        st["lens"].copy_(dev_i32(np.concatenate([lens[rows], np.zeros(pad)])))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = st["out"].clone()
+        assert np.all(host_bits(got[n:]) == 0), f"step {step}: padding rows not zero"
+        oracle.append(okp, ovp, case.table, kn_r, vn_r, case.slots[rows], lens[rows] - 1)
+        ref, _ = oracle.attn_decode(q_r, okp, ovp, case.table, case.slots[rows], lens[rows],
+                                    case.scale, 0)
+        assert_attn_close(host_f64(got[:n]), ref, f"step {step} (n={n}, bucket {nb})")
+        # the same rows unpadded, eager, tokens already appended: identical bits
+        e_out = pkv.attn_decode(dev_bits(q_r), dev_i32(case.slots[rows]), dev_i32(lens[rows]),
+                                table, kp, vp, scale=case.scale, max_seq_len_hint=hint)
+        torch.cuda.synchronize()
+        assert torch.equal(e_out.view(torch.int16), got[:n].view(torch.int16)), f"step {step}"
+    assert np.array_equal(host_bits(kp), okp) and np.array_equal(host_bits(vp), ovp)
