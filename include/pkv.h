@@ -212,7 +212,8 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t n_q_heads, int32_t n_kv_head
  *   scale      : softmax scale applied to q.k, finite and > 0
  *   lse        : device fp32 [total_tokens][n_q_heads] or NULL
  *   workspace  : unused by the current kernels (pass NULL / 0)
- * head_dim 512, pages_per_slot > 2048, n_seqs > 65535 and, with the
+ * head_dim 64, 128, 256 and 512 are supported (512: the Gemma-4
+ * full-attention layers).  pages_per_slot > 2048, n_seqs > 65535 and, with the
  * prologue, total_tokens > 2097120 are not supported here (PKV_ERR_UNSUPPORTED).
  */
 pkv_status pkv_attn_prefill(const void* q, int32_t n_q_heads, const int32_t* cu_seqlens,

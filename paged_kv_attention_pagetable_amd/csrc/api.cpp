@@ -291,7 +291,7 @@ pkv_status pkv_attn_prefill(const void* q, int32_t n_q_heads, const int32_t* cu_
   if (n_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "%s: n_seqs must be <= 65535", fn);
   pkv::PoolGeom g;
   pkv::TableRef tr;
-  pkv_status st = check_cache(fn, cd, pt, false, &g, &tr);
+  pkv_status st = check_cache(fn, cd, pt, true, &g, &tr);
   if (st != PKV_OK) return st;
   int G = 0;
   st = check_heads(fn, n_q_heads, g.n_kv, &G);

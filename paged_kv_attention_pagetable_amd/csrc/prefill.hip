@@ -54,6 +54,14 @@ template <int D>
 constexpr int prefill_threads() { return 64 * prefill_waves<D>(); }
 template <int D>
 constexpr int prefill_nt() { return D <= 128 ? 2 : 1; }
+// LDS tile buffers: two (the next chunk's copies in flight during the current
+// chunk's math), except at head_dim 512, whose 128 KB tile fits once.
+template <int D>
+constexpr int prefill_bufs() { return D == 512 ? 1 : 2; }
+// Waves per SIMD: two (256 registers each); head_dim 512 runs one workgroup
+// per CU (LDS) and so one wave per SIMD, with the 512-register budget.
+template <int D>
+constexpr int prefill_wpe() { return D == 512 ? 1 : 2; }
 
 template <int D>
 constexpr int k_tile_bytes() { return kChunk * D * 2; }   // [64 keys][D] bf16
@@ -660,13 +668,19 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, const SeqMeta& sm
     else norm_rope_q<D, NT, false>(a, quad, nullptr, wq);
   }
   if (it.n_chunks > 0 && zero_tail<D>(lds, 0, it.j_start, it.kv_hi, tid)) __syncthreads();
+  constexpr int NB = prefill_bufs<D>();
   for (int ck = 0; ck < it.n_chunks; ++ck) {
     const int j0 = it.j_start + ck * kChunk;
-    if (ck + 1 < it.n_chunks) issue_tile<D>(a, it, s_pg, lds, (ck + 1) & 1, j0 + kChunk, lc, lane, w);
-    chunk_math<D, NT>(a, lds, (ck & 1) * tile_bytes<D>(), j0, lc, wq, quad, inv_c, sa);
+    const int nbuf = (ck + 1) & (NB - 1);  // buffer of the next chunk
+    if (NB == 2 && ck + 1 < it.n_chunks) issue_tile<D>(a, it, s_pg, lds, nbuf, j0 + kChunk, lc, lane, w);
+    chunk_math<D, NT>(a, lds, (ck & (NB - 1)) * tile_bytes<D>(), j0, lc, wq, quad, inv_c, sa);
+    if (NB == 1 && ck + 1 < it.n_chunks) {
+      __syncthreads();  // every wave is done with the single buffer
+      issue_tile<D>(a, it, s_pg, lds, 0, j0 + kChunk, lc, lane, w);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk's copies have landed
     __syncthreads();
-    if (ck + 1 < it.n_chunks && zero_tail<D>(lds, (ck + 1) & 1, j0 + kChunk, it.kv_hi, tid))
+    if (ck + 1 < it.n_chunks && zero_tail<D>(lds, nbuf, j0 + kChunk, it.kv_hi, tid))
       __syncthreads();
   }
   store_out<D, NT>(a, it, w, lane, sa);
@@ -680,7 +694,7 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, const SeqMeta& sm
 // each keep their heads' K/V in their own L2.
 template <int D, int NT, bool RQ>
 __global__ __launch_bounds__(prefill_threads<D>())
-__attribute__((amdgpu_waves_per_eu(prefill_waves<D>() / 2, prefill_waves<D>() / 2)))
+__attribute__((amdgpu_waves_per_eu(prefill_wpe<D>(), prefill_wpe<D>())))
 void prefill_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int s_pg[kStagePages];
@@ -712,7 +726,7 @@ hipError_t set_lds_limit(K* kernel, int bytes) {
 template <int D>
 hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t st) {
   constexpr int NT = prefill_nt<D>();
-  const int lds = 2 * tile_bytes<D>();
+  const int lds = prefill_bufs<D>() * tile_bytes<D>();
   static const hipError_t attr0 = set_lds_limit(&prefill_kernel<D, NT, false>, lds);
   static const hipError_t attr1 = set_lds_limit(&prefill_kernel<D, NT, true>, lds);
   if (attr0 != hipSuccess) return attr0;
@@ -739,7 +753,8 @@ int prefill_q_tokens(int G, int head_dim) {
   switch (head_dim) {
     case 64: return prefill_waves<64>() * prefill_nt<64>() * 16 / G;
     case 128: return prefill_waves<128>() * prefill_nt<128>() * 16 / G;
-    default: return prefill_waves<256>() * prefill_nt<256>() * 16 / G;
+    case 256: return prefill_waves<256>() * prefill_nt<256>() * 16 / G;
+    default: return prefill_waves<512>() * prefill_nt<512>() * 16 / G;
   }
 }
 
@@ -748,6 +763,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
     case 64: return launch_prefill_d<64>(a, st);
     case 128: return launch_prefill_d<128>(a, st);
     case 256: return launch_prefill_d<256>(a, st);
+    case 512: return launch_prefill_d<512>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -355,6 +355,7 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t st) {
     case 64: return launch_prologue_d<64>(a, st);
     case 128: return launch_prologue_d<128>(a, st);
     case 256: return launch_prologue_d<256>(a, st);
+    case 512: return launch_prologue_d<512>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -94,8 +94,8 @@ def test_append_and_prefill_argument_checks():
     assert L.pkv_append(P, P, P, P, 0, _pt(), ctypes.byref(cd), P, P, None) == 0  # T = 0 no-op
     assert L.pkv_append(None, P, P, P, 5, _pt(), ctypes.byref(cd), P, P, None) == 1
     assert L.pkv_append(P, P, P, P, 5, _pt(), ctypes.byref(cd), P + 2, P, None) == 1  # misaligned pool
-    cd512 = _desc(D=512)
-    assert L.pkv_attn_prefill(P, 4, P, P, None, 1, 8, 8, _pt(), ctypes.byref(cd512), P, P,
+    cd96 = _desc(D=96)        # head_dim not supported (64, 128, 256, 512 are)
+    assert L.pkv_attn_prefill(P, 4, P, P, None, 1, 8, 8, _pt(), ctypes.byref(cd96), P, P,
                               0.1, 0, None, P, None, None, 0, None) == 2
     assert L.pkv_attn_prefill(None, 4, P, P, None, 1, 8, 8, _pt(), ctypes.byref(cd), P, P,
                               0.1, 0, None, P, None, None, 0, None) == 1

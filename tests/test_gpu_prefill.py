@@ -20,6 +20,9 @@ CASES = {
     "d128_g4_prefix": (32, 8, 128, 128, [40, 100, 3], [5, 128, 300], 0),
     "d128_g3": (24, 8, 128, 64, [70, 1, 200], None, 0),
     "d256_w64": (8, 2, 256, 64, [300, 45], [0, 20], 64),
+    # head_dim 512 (one LDS tile buffer, one wave per SIMD)
+    "d512_ragged": (8, 2, 512, 64, [70, 1, 130], None, 0),
+    "d512_prefix_w40_ps16": (16, 4, 512, 16, [50, 33], [20, 0], 40),
     "g1_ps16": (4, 4, 128, 16, [90, 31], None, 0),
     "g16": (16, 1, 64, 32, [40, 9], None, 0),
     "slot0_pad": (8, 2, 64, 16, [20, 12, 30], None, 0),
@@ -183,6 +186,7 @@ def _check_with_prologue(case, kp, vp, table, okp, ovp, name, hint=None):
 
 
 @pytest.mark.parametrize("name", ["tiny", "d128_g4_ragged", "d128_g4_prefix", "d256_w64",
+                                  "d512_ragged",
                                   "slot0_pad", "empty_prompts"])
 def test_prefill_with_prologue_matches_oracle(name):
     case = _case(name, seed=7)
@@ -251,12 +255,17 @@ def test_rope_table_partial_matches_fp64():
     assert np.all(c.cpu().numpy()[:, 64:] == 1.0) and np.all(s.cpu().numpy()[:, 64:] == 0.0)
 
 
-# Gemma-4 prologue variants: sliding layers (theta 1e4, window 64 here),
+# Gemma-4 prologue variants: sliding layers (head_dim 256, theta 1e4, window
+# 64 here), full-attention layers (head_dim 512, theta 1e6, 25 % rotary, K=V),
 # v_norm (RMSNorm without a gain) on v, K=V, and partial rotary.
-@pytest.mark.parametrize("k_eq_v,fraction", [(False, 1.0), (True, 1.0), (True, 0.25)])
-def test_prefill_with_gemma4_prologue(k_eq_v, fraction):
-    case = make_prefill_case(8, 2, 256, 64, [70, 33, 5], seed=2600 + int(k_eq_v),
-                             start_pos=[0, 40, 0], theta=1e4, window=64)
+@pytest.mark.parametrize("D,k_eq_v,fraction", [(256, False, 1.0), (256, True, 1.0),
+                                               (256, True, 0.25), (512, True, 0.25),
+                                               (512, False, 1.0)])
+def test_prefill_with_gemma4_prologue(D, k_eq_v, fraction):
+    full = D == 512
+    case = make_prefill_case(8, 2, D, 64, [70, 33, 5], seed=2600 + int(k_eq_v) + D,
+                             start_pos=[0, 40, 0], theta=1e6 if full else 1e4,
+                             window=0 if full else 64)
     kp, vp, table, okp, ovp = _pools_with_prefix(case)
     D = case.head_dim
     max_pos = int((case.start_pos + np.diff(case.cu_seqlens)).max()) + 1
