@@ -258,12 +258,9 @@ __device__ __forceinline__ void idle_output(const DecodeArgs& a, int b, int hk, 
 }
 
 // ---------------------------------------------------------------------------
-// head_dim <= 128: key split across the NW waves of the workgroup.
-// KLDS: K rows through the waves' LDS stages (splits of several chunks per
-// wave, where the HBM efficiency of the contiguous copies pays); otherwise
-// straight into operand registers (one chunk per wave: the extra LDS round
-// trip would sit on the critical path).
-template <int D, int NW, bool KLDS>
+// head_dim <= 128: key split across the NW waves of the workgroup (4, or 8
+// on short splits, see plan_decode); K rows through the waves' LDS stages.
+template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void decode_keysplit_kernel(DecodeArgs a) {
   // dynamic: the waves' K stages ([wave][32 keys][D] bf16) during the key
@@ -316,53 +313,36 @@ void decode_keysplit_kernel(DecodeArgs a) {
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) qreg[c] = load16(qrow + 32 * c);
     }
-    // A wave's chunk = 32 keys at t0.  K (KLDS): 1 KB global-to-LDS copies
-    // into the wave's stage (copy i, lane l: stage bytes 1024*i + 16*l = row
-    // r, slot u, filled from unit u ^ kst_swz(r) of key t0 + r).  Keys >= seg1
-    // read a row of page 0 or of the chunk's own page, always inside the pool;
-    // their scores are masked.  K (register path): the MFMA rows' 16-byte
-    // loads, zero past seg1.  V^T: 16-byte loads into operand registers,
+    // A wave's chunk = 32 keys at t0.  K: 1 KB global-to-LDS copies into the
+    // wave's stage (copy i, lane l: stage bytes 1024*i + 16*l = row r, slot
+    // u, filled from unit u ^ kst_swz(r) of key t0 + r).  Keys >= seg1 read a
+    // row of page 0 or of the chunk's own page, always inside the pool; their
+    // scores are masked.  V^T: 16-byte loads into operand registers,
     // zero for keys >= seg1 or on an unmapped page (0 * NaN would poison P.V).
     // No prefetch of the next chunk: the registers it would take buy a third
     // wave per SIMD instead, which keeps more bytes in flight per CU.
     uint8_t* kst = reinterpret_cast<uint8_t*>(s_o) + w * kStage;
     for (int t0 = seg0 + 32 * w; t0 < seg1; t0 += 32 * NW) {
-      u32x4 kop[2][D / 32];  // (register path)
-      if constexpr (KLDS) {
-        if (ps >= 32) {
-          // the chunk lies in one page (t0 < seg1): one scalar page id
-          const int pg = __builtin_amdgcn_readfirstlane(max(s_pg[(t0 >> log2ps) - p0], 0));
-          const bf16_t* ks = kbase + (size_t)pg * page_stride + (size_t)(t0 & (ps - 1)) * D;
+      if (ps >= 32) {
+        // the chunk lies in one page (t0 < seg1): one scalar page id
+        const int pg = __builtin_amdgcn_readfirstlane(max(s_pg[(t0 >> log2ps) - p0], 0));
+        const bf16_t* ks = kbase + (size_t)pg * page_stride + (size_t)(t0 & (ps - 1)) * D;
 #pragma unroll
-          for (int i = 0; i < kStage / 1024; ++i) {
-            const int o = 1024 * i + 16 * lane;
-            const int rr = o / (2 * D), u = ((o % (2 * D)) >> 4) ^ kst_swz<D>(o / (2 * D));
-            __builtin_amdgcn_global_load_lds(ks + rr * D + 8 * u, (lds_void_ptr)(kst + 1024 * i), 16, 0, kNtAux);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < kStage / 1024; ++i) {
-            const int o = 1024 * i + 16 * lane;
-            const int rr = o / (2 * D), u = ((o % (2 * D)) >> 4) ^ kst_swz<D>(o / (2 * D));
-            const int tk = t0 + rr;
-            const int pg = s_pg[min((tk >> log2ps) - p0, kSegPages - 1)];
-            const int page = tk < seg1 ? max(pg, 0) : 0;
-            __builtin_amdgcn_global_load_lds(kbase + (size_t)page * page_stride + (size_t)(tk & (ps - 1)) * D + 8 * u,
-                                             (lds_void_ptr)(kst + 1024 * i), 16, 0, kNtAux);
-          }
+        for (int i = 0; i < kStage / 1024; ++i) {
+          const int o = 1024 * i + 16 * lane;
+          const int rr = o / (2 * D), u = ((o % (2 * D)) >> 4) ^ kst_swz<D>(o / (2 * D));
+          __builtin_amdgcn_global_load_lds(ks + rr * D + 8 * u, (lds_void_ptr)(kst + 1024 * i), 16, 0, kNtAux);
         }
       } else {
-        // Keys past seg1 or on an unmapped page read page 0 (in the pool); no
-        // zeroing: their scores are masked by selection, and a NaN in a K row
-        // reaches only that key's scores.  (A select on the loaded value here
-        // would wait for each load before the rest are issued.)
 #pragma unroll
-        for (int rg = 0; rg < 2; ++rg) {
-          const int tk = t0 + 8 * (qc >> 2) + 4 * rg + (qc & 3);
-          const int page = tk < seg1 ? s_pg[(tk >> log2ps) - p0] : -1;
-          const bf16_t* kp = kbase + (size_t)max(page, 0) * page_stride + (size_t)(tk & (ps - 1)) * D + 8 * quad;
-#pragma unroll
-          for (int c = 0; c < D / 32; ++c) kop[rg][c] = load16_nt(kp + 32 * c);
+        for (int i = 0; i < kStage / 1024; ++i) {
+          const int o = 1024 * i + 16 * lane;
+          const int rr = o / (2 * D), u = ((o % (2 * D)) >> 4) ^ kst_swz<D>(o / (2 * D));
+          const int tk = t0 + rr;
+          const int pg = s_pg[min((tk >> log2ps) - p0, kSegPages - 1)];
+          const int page = tk < seg1 ? max(pg, 0) : 0;
+          __builtin_amdgcn_global_load_lds(kbase + (size_t)page * page_stride + (size_t)(tk & (ps - 1)) * D + 8 * u,
+                                           (lds_void_ptr)(kst + 1024 * i), 16, 0, kNtAux);
         }
       }
       const int tv = t0 + 8 * quad;
@@ -378,10 +358,8 @@ void decode_keysplit_kernel(DecodeArgs a) {
           vop[dt] = vpage >= 0 ? (nvalid < 8 ? keep_first(v, nvalid) : v) : u32x4{0, 0, 0, 0};
         }
       }
-      if constexpr (KLDS) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the K copies have landed in the stage
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // (and the stage reads stay after it)
-      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the K copies have landed in the stage
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);  // (and the stage reads stay after it)
       // ---- S^T = K Q^T; MFMA rg row m holds key 8*(m/4) + 4*rg + m%4
       f32x4 S[2];
 #pragma unroll
@@ -390,8 +368,7 @@ void decode_keysplit_kernel(DecodeArgs a) {
         f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) {
-          const u32x4 kv = KLDS ? *reinterpret_cast<const u32x4*>(kst + rr * (2 * D) + 16 * ((4 * c + quad) ^ kst_swz<D>(rr)))
-                                : kop[rg][c];
+          const u32x4 kv = *reinterpret_cast<const u32x4*>(kst + rr * (2 * D) + 16 * ((4 * c + quad) ^ kst_swz<D>(rr)));
           sacc = mfma16x16x32(kv, qreg[c], sacc);
         }
         S[rg] = sacc;
@@ -643,7 +620,7 @@ void decode_dimsplit_kernel(DecodeArgs a) {
 }
 
 // Dynamic LDS of the key-split kernel: the larger of the waves' K stages and
-// their fp32 outputs (at most 4 * 16 * 128 * 4 = 32 KB, or 64 KB with 8 waves).
+// their fp32 outputs (at most 64 KB: 8 waves * 32 keys * 128 * 2 bytes).
 template <int D>
 size_t keysplit_lds_bytes(int waves, int G) {
   const size_t stage = (size_t)waves * 32 * D * 2, outs = (size_t)waves * G * D * sizeof(float);
@@ -660,14 +637,11 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.g.n_kv, a.B, a.max_splits);
   if constexpr (D <= 128) {
     if (a.waves == 8)
-      hipLaunchKernelGGL((decode_keysplit_kernel<D, 8, true>), grid, dim3(8 * 64),
+      hipLaunchKernelGGL((decode_keysplit_kernel<D, 8>), grid, dim3(8 * 64),
                          keysplit_lds_bytes<D>(8, a.G), st, a);
-    else if (a.split_tokens > 32 * kDecodeWaves)
-      hipLaunchKernelGGL((decode_keysplit_kernel<D, kDecodeWaves, true>), grid, dim3(kThreads),
-                         keysplit_lds_bytes<D>(kDecodeWaves, a.G), st, a);
     else
-      hipLaunchKernelGGL((decode_keysplit_kernel<D, kDecodeWaves, false>), grid, dim3(kThreads),
-                         (size_t)kDecodeWaves * a.G * D * sizeof(float), st, a);
+      hipLaunchKernelGGL((decode_keysplit_kernel<D, kDecodeWaves>), grid, dim3(kThreads),
+                         keysplit_lds_bytes<D>(kDecodeWaves, a.G), st, a);
   } else
     hipLaunchKernelGGL((decode_dimsplit_kernel<D>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
@@ -694,12 +668,21 @@ DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_h
           ((range + split - 1) / split) * G > kMaxMergeUnits) &&
          split < (1 << 24))
     split *= 2;
+  // Short splits: when every wave of a 4-wave workgroup would get a single
+  // 32-key chunk, 8-wave workgroups over 256-key splits (half the workgroups,
+  // half the partials to merge) measured faster: Qwen3 shape 10.9 -> 10.2 us.
+  // Longer splits keep 4 waves (Llama shape: 97 us, against 112 with 8).
+  int waves = kDecodeWaves;
+  if (head_dim <= 128 && split == 32 * kDecodeWaves) {
+    waves = 8;
+    split = 32 * 8;
+  }
   p.split_tokens = (int)split;
   p.max_splits = (int)((range + split - 1) / split);
-  p.waves = kDecodeWaves;
+  p.waves = waves;
   // (One 8-wave workgroup per pair without a split was measured slower than
   // split + merge even for 8 rows: 64 CUs stream ~16 GB/s each with
-  // sequential chunks.  The 8-wave variant stays available to the launcher.)
+  // sequential chunks.)
   if (p.max_splits <= 1) {
     p.max_splits = 1;
     p.ws_bytes = 0;

@@ -54,10 +54,10 @@ def test_decode_matches_oracle(name):
 
 
 # A length hint far above the real lengths makes the splits long (several
-# 32-key chunks per wave), which routes head_dim <= 128 through the kernel
-# variant that copies K into LDS; the default hint keeps 128-key splits (K
-# loaded straight into operand registers).  With 100000 the splits are 256 to
-# 2048 keys, so the longer rows still have several splits to merge.
+# 32-key chunks per wave of 4-wave workgroups); the default hint of these
+# small cases gives 256-key splits over 8-wave workgroups (one chunk per
+# wave).  With 100000 the splits are 256 to 2048 keys, so the longer rows
+# still have several splits to merge.
 LONG_SPLIT_HINT = 1_000_000
 
 
