@@ -509,22 +509,23 @@ __device__ __forceinline__ void acc_init(SoftmaxAcc<D, NT>& s) {
 }
 
 // One 64-key chunk (keys j0 ..) from LDS buffer offset buf_off for this wave.
-template <int D, int NT>
-__device__ __forceinline__ void chunk_math(const PrefillArgs& a, const uint8_t* lds, int buf_off,
-                                           int j0, const LaneConst<D>& lc, const WaveQ<D, NT>& wq,
-                                           int quad, float inv_c, SoftmaxAcc<D, NT>& sa) {
-  const bool skip = wq.hi < 0 || j0 > wq.hi || (a.window > 0 && j0 + kChunk - 1 <= wq.lo - a.window);
-  if (skip) return;
-  const bool full = (j0 + kChunk - 1 <= wq.lo) && (a.window <= 0 || wq.hi - j0 < a.window);
+// NH = the 32-key halves that hold a key some query of this wave sees (1:
+// the second half lies past the wave's last query position, as in the last
+// chunk of every query block that starts at a multiple of 64; its MFMAs and
+// exponentials are skipped).
+template <int D, int NT, int NH>
+__device__ __forceinline__ void chunk_halves(const PrefillArgs& a, const uint8_t* lds, int buf_off,
+                                             int j0, const LaneConst<D>& lc, const WaveQ<D, NT>& wq,
+                                             int quad, float inv_c, bool full, SoftmaxAcc<D, NT>& sa) {
   // Scheduling hint for the QK^T block: the compiler's MFMA / LDS-read
   // interleaving strategy 1 (measured 44.8 -> 43.8 us on the Qwen3 prompts;
   // strategy 0, or the hint on the P.V blocks too, were slower).
   __builtin_amdgcn_iglp_opt(1);
   // ---- S^T = K Q^T for the chunk's two 32-key halves h: MFMA rg row m holds
   // key j0 + 32h + 8*(m/4) + 4*rg + m%4
-  f32x4 S[2][NT][2];
+  f32x4 S[NH][NT][2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < NH; ++h)
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg) {
 #pragma unroll
@@ -542,7 +543,7 @@ __device__ __forceinline__ void chunk_math(const PrefillArgs& a, const uint8_t* 
       const int pc = wq.pcol[nt];
       const int jmin = a.window > 0 ? pc - a.window + 1 : -0x7fffffff;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
@@ -561,7 +562,7 @@ __device__ __forceinline__ void chunk_math(const PrefillArgs& a, const uint8_t* 
   bool need = false;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    lmax[nt] = vmax(max8(S[0][nt]), max8(S[1][nt]));
+    lmax[nt] = NH == 2 ? vmax(max8(S[0][nt]), max8(S[NH - 1][nt])) : max8(S[0][nt]);
     need |= lmax[nt] > sa.thr[nt];
   }
   if (__any(need)) {
@@ -582,7 +583,7 @@ __device__ __forceinline__ void chunk_math(const PrefillArgs& a, const uint8_t* 
     }
   }
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < NH; ++h) {
     u32x4 pb[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -603,6 +604,19 @@ __device__ __forceinline__ void chunk_math(const PrefillArgs& a, const uint8_t* 
       for (int nt = 0; nt < NT; ++nt) sa.o[nt][dt] = mfma16x16x32(vv, pb[nt], sa.o[nt][dt]);
     }
   }
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void chunk_math(const PrefillArgs& a, const uint8_t* lds, int buf_off,
+                                           int j0, const LaneConst<D>& lc, const WaveQ<D, NT>& wq,
+                                           int quad, float inv_c, SoftmaxAcc<D, NT>& sa) {
+  const bool skip = wq.hi < 0 || j0 > wq.hi || (a.window > 0 && j0 + kChunk - 1 <= wq.lo - a.window);
+  if (skip) return;
+  const bool full = (j0 + kChunk - 1 <= wq.lo) && (a.window <= 0 || wq.hi - j0 < a.window);
+  if (j0 + 32 <= wq.hi)
+    chunk_halves<D, NT, 2>(a, lds, buf_off, j0, lc, wq, quad, inv_c, full, sa);
+  else
+    chunk_halves<D, NT, 1>(a, lds, buf_off, j0, lc, wq, quad, inv_c, full, sa);
 }
 
 // Normalise and store the wave's columns of an item (padding rows: 0 / -inf).
