@@ -352,10 +352,26 @@ pkv_status pkv_pt_export(const pkv_pt* pt, int32_t* table_out, int32_t pages_per
  * holds (PKV_RESERVE_TOO_LONG), or whose stored capacity is not a multiple of
  * page_size within the row (PKV_RESERVE_BAD_STATE) changes nothing, and the
  * rows after it proceed.  The slots of one call must be distinct (as for
- * decode).  allocate and erase stay on the host.
+ * decode).  Slot bookkeeping (allocate) stays on the host.
  *   slots, seq_lens : device int32 [B]; B == 0 is a no-op
  * Returns PKV_ERR_INVALID_ARG for NULL pointers or bad sizes (nothing
  * enqueued), PKV_ERR_LAUNCH if the launch fails.
+ *
+ * pkv_pt_device_erase(dev, slots, B, stream) applies, on `stream`, what B host
+ * calls erase(slots[b]) in row order would do to the pages
+ * ([continuous-batching compare] flex_paged_attention.py, PageTable.erase):
+ * the capacity / page_size pages a slot owns (its first table entries) are
+ * pushed back on the free stack in reverse logical order, after those of the
+ * rows before it.  Then, unlike the host erase, the slot's capacity is set to
+ * 0 and its table row to -1 (what the host allocate does on reuse), so the
+ * host may hand the slot out again, and reserve it on the device, with no
+ * further call.  Rows whose slot is outside [1, max_slots) are skipped; a row
+ * whose stored capacity is not a multiple of page_size within the row, or
+ * whose pages would overflow the n_pages entries of free_pages (a state that
+ * no sequence of allocator calls produces), changes nothing and sets
+ * PKV_RESERVE_BAD_STATE.  The slots of one call must be distinct.
+ *   slots : device int32 [B]; B == 0 is a no-op
+ * Returns as pkv_pt_device_reserve.
  */
 #define PKV_RESERVE_NO_PAGES 1u
 #define PKV_RESERVE_TOO_LONG 2u
@@ -374,6 +390,8 @@ typedef struct {
 
 pkv_status pkv_pt_device_reserve(const pkv_pt_device* dev, const int32_t* slots,
                                  const int32_t* seq_lens, int32_t B, void* stream);
+pkv_status pkv_pt_device_erase(const pkv_pt_device* dev, const int32_t* slots, int32_t B,
+                               void* stream);
 
 #ifdef __cplusplus
 }

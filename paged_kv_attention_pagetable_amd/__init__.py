@@ -305,7 +305,8 @@ class PageAllocator:
         return list(buf[:n])
 
     def to_device(self, pages_per_slot, device="cuda"):
-        """This allocator's state as a ``DevicePageState`` for device-side reserves."""
+        """This allocator's state as a ``DevicePageState`` for device-side reserves
+        and erases."""
         free = self.free_pages()
         fp = torch.zeros(self.n_pages, dtype=torch.int32)
         fp[:len(free)] = torch.tensor(free, dtype=torch.int32)
@@ -325,7 +326,8 @@ class PageAllocator:
 
 
 class DevicePageState:
-    """Device buffers of the allocator state used by ``pkv_pt_device_reserve``:
+    """Device buffers of the allocator state used by ``pkv_pt_device_reserve`` and
+    ``pkv_pt_device_erase``:
     ``table`` int32 [max_slots, pages_per_slot], ``free_pages`` int32 [n_pages]
     (the free stack, bottom first), ``free_count`` int32 [1], ``capacity``
     int32 [max_slots] and the ``status`` flag word (uint32 [1], as int32)."""
@@ -349,3 +351,11 @@ class DevicePageState:
         _i32(seq_lens, "seq_lens")
         check(lib().pkv_pt_device_reserve(ctypes.byref(self._c), _ptr(slots), _ptr(seq_lens),
                                           slots.numel(), _stream(stream, self.table.device)))
+
+    def erase(self, slots, stream=None):
+        """Return the pages of the listed slots (in order) to the free stack on the
+        device and reset their capacity to 0 and rows to -1
+        (``pkv_pt_device_erase``)."""
+        _i32(slots, "slots")
+        check(lib().pkv_pt_device_erase(ctypes.byref(self._c), _ptr(slots), slots.numel(),
+                                        _stream(stream, self.table.device)))

@@ -92,6 +92,7 @@ _SIGS = {
     "pkv_pt_export": (c_int32, [c_void_p, ctypes.POINTER(c_int32), c_int32]),
     "pkv_pt_device_reserve": (c_int32, [ctypes.POINTER(PtDevice), c_void_p, c_void_p, c_int32,
                                         c_void_p]),
+    "pkv_pt_device_erase": (c_int32, [ctypes.POINTER(PtDevice), c_void_p, c_int32, c_void_p]),
 }
 
 _lib = None

@@ -122,9 +122,13 @@ pkv_status pkv_validation_flags(uint32_t* flags, int32_t clear, void* stream) {
   return PKV_OK;
 }
 
-pkv_status pkv_pt_device_reserve(const pkv_pt_device* dev, const int32_t* slots,
-                                 const int32_t* seq_lens, int32_t B, void* stream) {
-  const char* fn = "pkv_pt_device_reserve";
+}  // extern "C"
+
+namespace {
+
+// Shared argument checks and marshalling of the device allocator calls.
+pkv_status device_state_args(const char* fn, const pkv_pt_device* dev, const int32_t* slots,
+                             int32_t B, pkv::ReserveArgs* a) {
   if (!dev) return fail(PKV_ERR_INVALID_ARG, "%s: NULL state", fn);
   if (B < 0) return fail(PKV_ERR_INVALID_ARG, "%s: B must be >= 0 (got %d)", fn, B);
   if (dev->max_slots < 2 || dev->pages_per_slot < 1 || dev->page_size < 1 || dev->n_pages < 2)
@@ -134,22 +138,46 @@ pkv_status pkv_pt_device_reserve(const pkv_pt_device* dev, const int32_t* slots,
     return fail(PKV_ERR_INVALID_ARG, "%s: pages_per_slot * page_size exceeds 2^30 tokens", fn);
   if (!dev->table || !dev->free_pages || !dev->free_count || !dev->capacity || !dev->status)
     return fail(PKV_ERR_INVALID_ARG, "%s: NULL state buffer", fn);
-  if (B == 0) return PKV_OK;
-  if (!slots || !seq_lens) return fail(PKV_ERR_INVALID_ARG, "%s: NULL slots or seq_lens", fn);
+  if (B > 0 && !slots) return fail(PKV_ERR_INVALID_ARG, "%s: NULL slots", fn);
+  a->table = dev->table;
+  a->free_pages = dev->free_pages;
+  a->free_count = dev->free_count;
+  a->capacity = dev->capacity;
+  a->status = dev->status;
+  a->slots = slots;
+  a->seq_lens = nullptr;
+  a->B = B;
+  a->max_slots = dev->max_slots;
+  a->pps = dev->pages_per_slot;
+  a->page_size = dev->page_size;
+  a->n_pages = dev->n_pages;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_pt_device_reserve(const pkv_pt_device* dev, const int32_t* slots,
+                                 const int32_t* seq_lens, int32_t B, void* stream) {
+  const char* fn = "pkv_pt_device_reserve";
   pkv::ReserveArgs a;
-  a.table = dev->table;
-  a.free_pages = dev->free_pages;
-  a.free_count = dev->free_count;
-  a.capacity = dev->capacity;
-  a.status = dev->status;
-  a.slots = slots;
+  const pkv_status st = device_state_args(fn, dev, slots, B, &a);
+  if (st != PKV_OK) return st;
+  if (B == 0) return PKV_OK;
+  if (!seq_lens) return fail(PKV_ERR_INVALID_ARG, "%s: NULL slots or seq_lens", fn);
   a.seq_lens = seq_lens;
-  a.B = B;
-  a.max_slots = dev->max_slots;
-  a.pps = dev->pages_per_slot;
-  a.page_size = dev->page_size;
-  a.n_pages = dev->n_pages;
   return launched(pkv::launch_reserve(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+pkv_status pkv_pt_device_erase(const pkv_pt_device* dev, const int32_t* slots, int32_t B,
+                               void* stream) {
+  const char* fn = "pkv_pt_device_erase";
+  pkv::ReserveArgs a;
+  const pkv_status st = device_state_args(fn, dev, slots, B, &a);
+  if (st != PKV_OK) return st;
+  if (B == 0) return PKV_OK;
+  return launched(pkv::launch_erase(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 size_t pkv_prefill_workspace_size(int32_t total_tokens, int32_t n_seqs, int32_t n_q_heads) {

@@ -140,7 +140,8 @@ hipError_t launch_validate_tokens(const TableRef& pt, const PoolGeom& g, const i
                                   const int32_t* pos, int T, hipStream_t st);
 hipError_t read_validate_flags(uint32_t* host_out, int clear, hipStream_t st);
 
-// Device-side batch reserve (see pkv_pt_device_reserve in the public header).
+// Device-side batch reserve and erase (see pkv_pt_device_reserve and
+// pkv_pt_device_erase in the public header).
 struct ReserveArgs {
   int32_t* table;
   int32_t* free_pages;
@@ -155,6 +156,7 @@ constexpr uint32_t kReserveNoPages = 1u;
 constexpr uint32_t kReserveTooLong = 2u;
 constexpr uint32_t kReserveBadState = 4u;
 hipError_t launch_reserve(const ReserveArgs& a, hipStream_t st);
+hipError_t launch_erase(const ReserveArgs& a, hipStream_t st);  // seq_lens unused
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);

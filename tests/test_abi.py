@@ -231,3 +231,18 @@ def test_device_reserve_argument_checks():
                 _lib.PtDevice(None, P, P, P, P, 9, 8, 128, 100),
                 _lib.PtDevice(P, P, P, P, None, 9, 8, 128, 100)):
         assert L.pkv_pt_device_reserve(ctypes.byref(bad), P, P, 4, None) == 1
+
+
+def test_device_erase_argument_checks():
+    L = pkv.lib()
+    ok = _lib.PtDevice(P, P, P, P, P, 9, 8, 128, 100)
+    assert L.pkv_pt_device_erase(None, P, 4, None) == 1
+    assert L.pkv_pt_device_erase(ctypes.byref(ok), P, -1, None) == 1
+    assert L.pkv_pt_device_erase(ctypes.byref(ok), P, 0, None) == 0      # no-op
+    assert L.pkv_pt_device_erase(ctypes.byref(ok), None, 4, None) == 1
+    for bad in (_lib.PtDevice(P, P, P, P, P, 1, 8, 128, 100),
+                _lib.PtDevice(P, P, P, P, P, 9, 8, 128, 1),
+                _lib.PtDevice(P, P, P, None, P, 9, 8, 128, 100),
+                _lib.PtDevice(P, P, P, P, P, 9, 1 << 25, 64, 100)):      # 2^31 tokens per row
+        assert L.pkv_pt_device_erase(ctypes.byref(bad), P, 4, None) == 1
+        assert "pkv_pt_device_erase" in pkv.lib().pkv_last_error().decode()

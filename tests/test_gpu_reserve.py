@@ -200,3 +200,124 @@ def test_graph_decode_step_reserves_pages_on_device():
             assert_attn_close(got[b], ref, f"replay {it} row {b}")
         _model_batch(m, pps, slots, lens)
     _compare(st, m, pps, 0)
+
+
+def _model_erase(m, slots):
+    """The device erase on the model: the pages' erase of each listed slot in
+    order, then the reset the allocate of each does (capacity 0, row -1)."""
+    done = [int(s) for s in slots if 1 <= int(s) < m.max_slots]
+    for s in done:
+        m.erase(s)
+    for _ in done:
+        m.allocate()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_device_erase_matches_model(seed):
+    rng = np.random.default_rng(150 + seed)
+    ps = int(rng.choice([16, 64, 128]))
+    n_pages, max_slots, pps = int(rng.integers(40, 200)), int(rng.integers(4, 40)), 16
+    m, live = _history(rng, n_pages, ps, max_slots, pps, steps=60)
+    st = _to_device(m, pps)
+    k = int(rng.integers(1, len(live) + 1))
+    gone = [int(s) for s in rng.choice(live, size=k, replace=False)]
+    rows = gone + [0, max_slots]          # padding and out-of-range rows are skipped
+    rows = [rows[i] for i in rng.permutation(len(rows))]
+    st.erase(dev_i32(rows))
+    _model_erase(m, rows)
+    _compare(st, m, pps, 0)
+    # the freed pages are granted again, in stack order, by a device reserve
+    lens = [int(rng.integers(1, pps * ps + 1)) for _ in gone]
+    st.reserve(dev_i32(gone), dev_i32(lens))
+    flags = _model_batch(m, pps, gone, lens)
+    _compare(st, m, pps, flags)
+
+
+def test_device_erase_many_rows_across_tiles():
+    """Erase 450 of 600 slots (two 256-row tiles), then reserve them again."""
+    rng = np.random.default_rng(19)
+    ps, pps = 16, 8
+    m = PageTableModel(5000, ps, 601)
+    slots = [m.allocate() for _ in range(600)]
+    for s, L in zip(slots, rng.integers(0, pps * ps + 1, size=600)):
+        m.reserve(s, int(L))
+    st = _to_device(m, pps)
+    gone = [int(s) for s in rng.permutation(slots)[:450]]
+    st.erase(dev_i32(gone))
+    _model_erase(m, gone)
+    _compare(st, m, pps, 0)
+    lens = [int(x) for x in rng.integers(0, pps * ps + 1, size=450)]
+    st.reserve(dev_i32(gone), dev_i32(lens))
+    flags = _model_batch(m, pps, gone, lens)
+    _compare(st, m, pps, flags)
+
+
+def test_device_erase_flags_inconsistent_state():
+    """States no allocator sequence produces: a capacity that is not a whole
+    number of pages, and owned pages that would overflow the free stack.  The
+    row is left unchanged, flagged, and the rows after it proceed."""
+    ps, pps, n_pages, max_slots = 16, 4, 10, 5
+    table = np.full((max_slots, pps), -1, np.int32)
+    table[0] = 0
+    table[1, :3] = [7, 8, 9]
+    table[2, :1] = [5]
+    table[3, :2] = [3, 4]
+    cap = np.array([0, 3 * ps, ps, 2 * ps - 1, 0], np.int32)
+    free = np.zeros(n_pages, np.int32)
+    free[:8] = [1, 2, 6, 1, 2, 6, 1, 2]       # 8 entries: slot 1's 3 pages cannot fit
+    st = pkv.DevicePageState(dev_i32(table), dev_i32(free), dev_i32([8]), dev_i32(cap), ps)
+    st.erase(dev_i32([1, 3, 2]))
+    torch.cuda.synchronize()
+    assert int(st.status.item()) == pkv.RESERVE_BAD_STATE
+    assert int(st.free_count.item()) == 9
+    got_free = st.free_pages.cpu().numpy()
+    assert got_free[8] == 5 and np.array_equal(got_free[:8], free[:8])
+    t = st.table.cpu().numpy()
+    want = table.copy()
+    want[2] = -1
+    assert np.array_equal(t, want)
+    assert np.array_equal(st.capacity.cpu().numpy(), [0, 3 * ps, 0, 2 * ps - 1, 0])
+
+
+def test_graph_step_erases_and_reserves_on_device():
+    """A captured step that erases the finished slots and then grows the live
+    ones, replayed with new inputs each time, matches the model after every
+    replay (no host round trip inside the step)."""
+    rng = np.random.default_rng(23)
+    ps, pps, max_slots, n_pages = 16, 8, 9, 96
+    m = PageTableModel(n_pages, ps, max_slots)
+    slots = [m.allocate() for _ in range(8)]
+    lens = [int(x) for x in rng.integers(1, 3 * ps, size=8)]
+    for s, L in zip(slots, lens):
+        m.reserve(s, L)
+    st = _to_device(m, pps)
+    d_gone = dev_i32([0] * 8)
+    d_slots = dev_i32(slots)
+    d_lens = dev_i32(lens)
+
+    def step():
+        st.erase(d_gone)
+        st.reserve(d_slots, d_lens)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    flags = 0
+    for it in range(12):
+        # a few slots finish (row slot, else 0 = padding) and restart short
+        gone = [s_ if rng.random() < 0.25 else 0 for s_ in slots]
+        lens = [int(rng.integers(1, ps)) if g_ else L + int(rng.integers(0, ps))
+                for g_, L in zip(gone, lens)]
+        lens = [min(L, pps * ps) for L in lens]
+        d_gone.copy_(dev_i32(gone))
+        d_lens.copy_(dev_i32(lens))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _model_erase(m, gone)
+        flags |= _model_batch(m, pps, slots, lens)
+        _compare(st, m, pps, flags)
