@@ -50,10 +50,20 @@ def log(msg):
 # workloads
 # ----------------------------------------------------------------------------
 
+def contiguous_table(table):
+    """The same page table with each slot's mapped logical pages renumbered to
+    consecutive physical pages (slot by slot, from page 1): the layout of a
+    cache whose pages were granted in order, to time the page indirection."""
+    t = table.copy()
+    rows, cols = np.nonzero(t[1:] > 0)
+    t[1:][rows, cols] = np.arange(1, len(rows) + 1, dtype=t.dtype)
+    return t
+
+
 class DecodeWorkload:
     """Per-layer pools with history already appended; one shared page table."""
 
-    def __init__(self, name, device="cuda"):
+    def __init__(self, name, device="cuda", contiguous=False):
         import torch
 
         import paged_kv_attention_pagetable_amd as pkv
@@ -73,6 +83,8 @@ class DecodeWorkload:
         base = make_decode_case(c["n_q"], c["n_kv"], kinds[0][0], ps, lengths,
                                 max_slots=c["max_slots"], seed=3407 + c["index"],
                                 slot_of_row=slots, pages_per_slot=pps, with_history=False)
+        if contiguous:
+            base.table = contiguous_table(base.table)
         self.case = base
         self.hint = c["len_hi"]
         dev = device
@@ -150,7 +162,7 @@ class DecodeWorkload:
 
 
 class PrefillWorkload:
-    def __init__(self, device="cuda"):
+    def __init__(self, device="cuda", contiguous=False):
         import torch
 
         import paged_kv_attention_pagetable_amd as pkv
@@ -165,6 +177,8 @@ class PrefillWorkload:
         case = make_prefill_case(c["n_q"], c["n_kv"], D, ps, lengths, seed=3407 + c["index"],
                                  slots=slots, max_slots=c["max_slots"],
                                  pages_per_slot=-(-c["len_hi"] // ps))
+        if contiguous:
+            case.table = contiguous_table(case.table)
         self.case = case
         dev = device
         self.table = torch.from_numpy(case.table).to(dev)
@@ -574,6 +588,9 @@ def main():
     ap.add_argument("--workload", default="qwen3_decode",
                     choices=["qwen3_decode", "llama_decode", "gemma_mixed"])
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--contiguous-pages", action="store_true",
+                    help="map each slot's pages to consecutive physical pages instead of a "
+                         "random permutation (times the page indirection)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel-reps", type=int, default=20,
@@ -616,7 +633,7 @@ def main():
     pkv.lib()
 
     log(f"setting up {args.workload}")
-    wl = DecodeWorkload(args.workload)
+    wl = DecodeWorkload(args.workload, contiguous=args.contiguous_pages)
     g_step = capture(wl.step)
     g_attn = capture(wl.attn_only)
     log("timing decode step")
@@ -629,6 +646,8 @@ def main():
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = (sum(attn_bytes) / wl.n_calls) / (ms_attn * 1e-3) / 1e9
     traffic = pmc_traffic(f"decode_{args.workload}", PMC_PARTS["decode"][1])
+    if args.contiguous_pages:
+        traffic = None   # the committed counters were taken on permuted tables
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                     kernel="decode attention (split-K kernel, last split merges)",
@@ -638,7 +657,8 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16, random page permutation)",
+        "data": "synthetic (seeded N(0,1) bf16, "
+                + ("contiguous pages)" if args.contiguous_pages else "random page permutation)"),
         "config": wl.describe(), "roofline": roofline,
         "step_ms_median": round(float(np.median(each)), 4), "step_ms_best": round(min(each), 4),
     }
@@ -654,7 +674,7 @@ def main():
 
     if not args.no_prefill:
         log("setting up qwen3_prefill")
-        pw = PrefillWorkload()
+        pw = PrefillWorkload(contiguous=args.contiguous_pages)
         gp_step = capture(pw.step)
         gp_attn = capture(pw.attn_only)
         log("timing prefill")
@@ -671,7 +691,8 @@ def main():
             "roofline": dict(bound="mfma", achieved=round(tflops, 2),
                              peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                              frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                             traffic=pmc_traffic("prefill_qwen3_prefill", PMC_PARTS["prefill"][1]),
+                             traffic=None if args.contiguous_pages else
+                             pmc_traffic("prefill_qwen3_prefill", PMC_PARTS["prefill"][1]),
                              kernel="prefill attention",
                              algorithmic_flops_per_call=fl, us_per_call=round(ms_pa * 1e3, 3)),
             "prologue_bytes_per_call": pw.prologue_bytes(),
