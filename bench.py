@@ -246,7 +246,8 @@ def reserve_timing(wl, calls=16, reps=8):
     """Device-side page reservation (pkv_pt_device_reserve) for the decode batch:
     us per call when every row with a slot takes one new page.  The state comes
     from the library's host allocator; it is restored before each timed replay of
-    a graph of `calls` reserves (call i grows each row to i more pages)."""
+    a graph of `calls` reserves (call i grows each row to i more pages).  Also
+    the device erase (pkv_pt_device_erase) of the same rows' slots."""
     import torch
     pkv, case = wl.pkv, wl.case
     ps = case.page_size
@@ -290,10 +291,41 @@ def reserve_timing(wl, calls=16, reps=8):
         torch.cuda.synchronize()
         times.append(a.elapsed_time(b) / calls * 1e3)
     assert int(st.status.item()) == 0, "device reserve reported a failure"
+    # the erase of every row's slot (pages back on the free stack): a graph of
+    # `calls` erases, each on its own copy of the allocator state
+    copies = [alloc.to_device(pps) for _ in range(calls)]
+    saved_c = [[t.clone() for t in (c.table, c.free_pages, c.free_count, c.capacity)]
+               for c in copies]
+
+    def restore_copies():
+        for c, sv in zip(copies, saved_c):
+            for t, t0 in zip((c.table, c.free_pages, c.free_count, c.capacity), sv):
+                t.copy_(t0)
+
+    torch.cuda.synchronize()
+    ge = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ge):
+        for c in copies:
+            c.erase(d_slots)
+    erase_times = []
+    for _ in range(reps):
+        restore_copies()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        ge.replay()
+        b.record()
+        torch.cuda.synchronize()
+        erase_times.append(a.elapsed_time(b) / calls * 1e3)
+    st = copies[-1]
+    assert int(st.status.item()) == 0, "device erase reported a failure"
+    assert int(st.capacity.sum().item()) == 0
     del got
     return dict(us_per_call=round(float(np.median(times)), 3), rows=len(slots),
                 pages_per_call=sum(1 for s in slots if s > 0),
-                kernel="device page reserve (pkv_pt_device_reserve, one workgroup)")
+                kernel="device page reserve (pkv_pt_device_reserve, one workgroup)",
+                erase_us_per_call=round(float(np.median(erase_times)), 3),
+                erase_pages=int(sum(-(-int(cap[s]) // ps) for s in slots if s > 0)))
 
 
 def capture(fn):
