@@ -321,3 +321,76 @@ def test_graph_step_erases_and_reserves_on_device():
         _model_erase(m, gone)
         flags |= _model_batch(m, pps, slots, lens)
         _compare(st, m, pps, flags)
+
+
+def test_slot_reuse_after_device_erase_decodes_correctly():
+    """Requests finish and new ones take over their slots with the device
+    allocator only: erase returns the pages, reserve hands the same (recycled)
+    pages to the new request, whose history is appended over the old one's.
+    Decode with the fused append must see only the new request's keys, even
+    though the recycled pages still hold the old request's rows past them."""
+    n_q, n_kv, D, ps = 8, 2, 128, 16
+    B, max_slots, n_pages, pps = 3, 4, 16, 8
+    rng = np.random.default_rng(91)
+    bf = lambda x: oracle.f64_to_bf16_bits(np.asarray(x, np.float64))
+    m = PageTableModel(n_pages, ps, max_slots)
+    slots = [m.allocate() for _ in range(B)]
+    st = _to_device(m, pps)
+    kp, vp = pkv.new_pools(n_pages, n_kv, ps, D, fill=-1)   # NaN sentinel
+    hist_k, hist_v = [None] * B, [None] * B
+    ws = pkv.new_decode_workspace(pkv.decode_workspace_size(B, n_q, n_kv, D, pps * ps), DEV)
+    d_slots = dev_i32(slots)
+
+    def start(rows, lengths):
+        """New requests on these rows: device reserve, then their history appended."""
+        lens = [0] * B
+        for b, L in zip(rows, lengths):
+            lens[b] = L
+        st.reserve(dev_i32([slots[b] for b in rows]), dev_i32(lengths))
+        flags = _model_batch(m, pps, [slots[b] for b in rows], lengths)
+        assert flags == 0
+        ks, vs, ts, tp = [], [], [], []
+        for b, L in zip(rows, lengths):
+            k = bf(rng.standard_normal((L, n_kv, D)))
+            v = bf(rng.standard_normal((L, n_kv, D)))
+            hist_k[b], hist_v[b] = oracle.bf16_bits_to_f64(k), oracle.bf16_bits_to_f64(v)
+            ks.append(k)
+            vs.append(v)
+            ts.append(np.full(L, slots[b], np.int32))
+            tp.append(np.arange(L, dtype=np.int32))
+        pkv.append(dev_bits(np.concatenate(ks)), dev_bits(np.concatenate(vs)),
+                   dev_i32(np.concatenate(ts)), dev_i32(np.concatenate(tp)), st.table, kp, vp)
+
+    def decode_steps(n):
+        for _ in range(n):
+            lens = [h.shape[0] + 1 for h in hist_k]
+            st.reserve(d_slots, dev_i32(lens))
+            assert _model_batch(m, pps, slots, lens) == 0
+            qb = bf(rng.standard_normal((B, n_q, D)))
+            kb = bf(rng.standard_normal((B, n_kv, D)))
+            vb = bf(rng.standard_normal((B, n_kv, D)))
+            out = pkv.attn_decode(dev_bits(qb).view(torch.bfloat16), d_slots, dev_i32(lens),
+                                  st.table, kp, vp, window=0, max_seq_len_hint=pps * ps,
+                                  k_new=dev_bits(kb).view(torch.bfloat16),
+                                  v_new=dev_bits(vb).view(torch.bfloat16), workspace=ws)
+            got = host_f64(out)
+            for b in range(B):
+                hist_k[b] = np.concatenate([hist_k[b], oracle.bf16_bits_to_f64(kb[b:b + 1])])
+                hist_v[b] = np.concatenate([hist_v[b], oracle.bf16_bits_to_f64(vb[b:b + 1])])
+                ref, _ = oracle.attend_rows(oracle.bf16_bits_to_f64(qb[b]), hist_k[b],
+                                            hist_v[b], lens[b] - 1, 1.0 / np.sqrt(D), 0)
+                assert_attn_close(got[b], ref, f"row {b} length {lens[b]}")
+
+    start([0, 1, 2], [40, 70, 20])         # 3 + 5 + 2 of the 15 pages
+    decode_steps(3)
+    # row 1 finishes; a shorter request takes its slot and recycled pages
+    st.erase(dev_i32([slots[1]]))
+    _model_erase(m, [slots[1]])
+    start([1], [23])
+    decode_steps(3)
+    # rows 0 and 2 finish; longer requests reuse pages row 1's first request held
+    st.erase(dev_i32([slots[0], slots[2]]))
+    _model_erase(m, [slots[0], slots[2]])
+    start([0, 2], [51, 33])
+    decode_steps(4)
+    _compare(st, m, pps, 0)
