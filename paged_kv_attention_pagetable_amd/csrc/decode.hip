@@ -87,10 +87,11 @@ struct RowRange {
   bool idle;
 };
 
-__device__ __forceinline__ RowRange row_range(const DecodeArgs& a, int b, int s) {
+__device__ __forceinline__ RowRange row_range(const DecodeArgs& a, int b, int s,
+                                               const int32_t* slots, const int32_t* seq_lens) {
   RowRange r;
-  r.slot = a.slots[b];
-  r.L = a.seq_lens[b];
+  r.slot = slots[b];
+  r.L = seq_lens[b];
   r.idle = r.slot <= 0 || r.slot >= a.pt.max_slots || r.L <= 0;
   r.lo = r.start = r.end = r.n_valid = 0;
   if (r.idle) return r;
@@ -262,7 +263,11 @@ __device__ __forceinline__ void idle_output(const DecodeArgs& a, int b, int hk, 
 // on short splits, see plan_decode); K rows through the waves' LDS stages.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3)))
-void decode_keysplit_kernel(DecodeArgs a) {
+void decode_keysplit_kernel(const int32_t* slots, const int32_t* seq_lens, const int32_t* table,
+                            int max_splits, DecodeArgs a) {
+  // slots .. max_splits repeat fields of `a`: passed first, they arrive
+  // preloaded in scalar registers (the library builds this file with four
+  // preloaded kernel arguments), so the slot and length loads issue at once.
   // dynamic: the waves' K stages ([wave][32 keys][D] bf16) during the key
   // loop, then the waves' outputs s_o ([wave][G][D] fp32) for the merge
   extern __shared__ __attribute__((aligned(16))) float s_o[];
@@ -270,11 +275,11 @@ void decode_keysplit_kernel(DecodeArgs a) {
   __shared__ float s_ml[2 * NW * 16];             // [wave][16] max, then sum
   __shared__ float s_red[NW * 16 + 32];
   constexpr int kStage = 32 * D * 2;              // bytes of a wave's K stage
-  const int hk = blockIdx.x, b = blockIdx.y, s = a.max_splits - 1 - (int)blockIdx.z;
+  const int hk = blockIdx.x, b = blockIdx.y, s = max_splits - 1 - (int)blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int qc = lane & 15, quad = lane >> 4;
   const int G = a.G;
-  const RowRange r = row_range(a, b, s);
+  const RowRange r = row_range(a, b, s, slots, seq_lens);
   if (r.idle) {
     idle_output(a, b, hk, s, D);
     return;
@@ -283,7 +288,7 @@ void decode_keysplit_kernel(DecodeArgs a) {
   if (a.k_new && r.end == r.L) append_new_token(a, r, b, hk, D);
 
   const int ps = a.g.page_size, log2ps = a.g.log2ps;
-  const int32_t* trow = a.pt.table + (size_t)r.slot * a.pt.pps;
+  const int32_t* trow = table + (size_t)r.slot * a.pt.pps;
   const size_t blk = (size_t)ps * D;
   const size_t page_stride = (size_t)a.g.n_kv * blk;
   const int lgv = min(log2ps, kLog2VGroup);  // log2 of the V key-group size
@@ -473,7 +478,7 @@ void decode_dimsplit_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int qc = lane & 15, quad = lane >> 4;
   const int G = a.G;
-  const RowRange r = row_range(a, b, s);
+  const RowRange r = row_range(a, b, s, a.slots, a.seq_lens);
   if (r.idle) {
     idle_output(a, b, hk, s, D);
     return;
@@ -638,10 +643,12 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t st) {
   if constexpr (D <= 128) {
     if (a.waves == 8)
       hipLaunchKernelGGL((decode_keysplit_kernel<D, 8>), grid, dim3(8 * 64),
-                         keysplit_lds_bytes<D>(8, a.G), st, a);
+                         keysplit_lds_bytes<D>(8, a.G), st, a.slots, a.seq_lens, a.pt.table,
+                         a.max_splits, a);
     else
       hipLaunchKernelGGL((decode_keysplit_kernel<D, kDecodeWaves>), grid, dim3(kThreads),
-                         keysplit_lds_bytes<D>(kDecodeWaves, a.G), st, a);
+                         keysplit_lds_bytes<D>(kDecodeWaves, a.G), st, a.slots, a.seq_lens,
+                         a.pt.table, a.max_splits, a);
   } else
     hipLaunchKernelGGL((decode_dimsplit_kernel<D>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
