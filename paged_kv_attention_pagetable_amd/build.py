@@ -31,13 +31,15 @@ COMMON = [
 ]
 
 
-# Per-source flags.  decode.hip: the key-split kernel takes its first four
-# arguments (slots, seq_lens, page table, split count) ahead of its argument
-# struct so that they arrive preloaded in scalar registers, and each
-# workgroup's first loads (its row's slot and length) issue without waiting
-# for an argument load.
+# Per-source flags.  The decode kernels take their first four arguments
+# (slots, seq_lens, page table, split count) and the prefill kernel its first
+# five (cu_seqlens, slots, start_pos, page table, sequence count) ahead of
+# their argument structs, so that these arrive preloaded in scalar registers
+# and each workgroup's first loads (its row's or sequence's metadata) issue
+# without waiting for an argument load.
 PER_SOURCE = {
     "decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=4"],
+    "prefill.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=5"],
 }
 
 

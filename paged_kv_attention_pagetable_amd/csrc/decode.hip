@@ -463,7 +463,9 @@ void decode_keysplit_kernel(const int32_t* slots, const int32_t* seq_lens, const
 // register double buffer, and four or five waves per SIMD, were slower).
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
-void decode_dimsplit_kernel(DecodeArgs a) {
+void decode_dimsplit_kernel(const int32_t* slots, const int32_t* seq_lens, const int32_t* table,
+                            int max_splits, DecodeArgs a) {
+  // preloaded repeats of fields of `a`, as in the key-split kernel
   constexpr int DW = D / kDecodeWaves;  // dims per wave
   constexpr int kStage = 32 * DW * 2;   // bytes of a wave's K stage
   static_assert(kDecodeWaves * kStage >= kMaxGD * (int)sizeof(float), "s_o must fit the stages");
@@ -474,11 +476,11 @@ void decode_dimsplit_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_stage[kDecodeWaves * kStage];
   float* const s_o = reinterpret_cast<float*>(s_stage);
   __shared__ float s_ml[32];
-  const int hk = blockIdx.x, b = blockIdx.y, s = a.max_splits - 1 - (int)blockIdx.z;
+  const int hk = blockIdx.x, b = blockIdx.y, s = max_splits - 1 - (int)blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int qc = lane & 15, quad = lane >> 4;
   const int G = a.G;
-  const RowRange r = row_range(a, b, s, a.slots, a.seq_lens);
+  const RowRange r = row_range(a, b, s, slots, seq_lens);
   if (r.idle) {
     idle_output(a, b, hk, s, D);
     return;
@@ -490,7 +492,7 @@ void decode_dimsplit_kernel(DecodeArgs a) {
   u32x4 qreg[DW / 32];  // loaded after the first page staging (see the key-split kernel)
   const bf16_t* qrow = a.q + ((size_t)b * a.n_q + hk * G + min(qc, G - 1)) * D + dw0 + 8 * quad;
   const int ps = a.g.page_size, log2ps = a.g.log2ps;
-  const int32_t* trow = a.pt.table + (size_t)r.slot * a.pt.pps;
+  const int32_t* trow = table + (size_t)r.slot * a.pt.pps;
   const size_t blk = (size_t)ps * D;
   const size_t page_stride = (size_t)a.g.n_kv * blk;
   const int lgv = min(log2ps, kLog2VGroup);  // log2 of the V key-group size
@@ -650,7 +652,8 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t st) {
                          keysplit_lds_bytes<D>(kDecodeWaves, a.G), st, a.slots, a.seq_lens,
                          a.pt.table, a.max_splits, a);
   } else
-    hipLaunchKernelGGL((decode_dimsplit_kernel<D>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_dimsplit_kernel<D>), grid, dim3(kThreads), 0, st, a.slots, a.seq_lens,
+                       a.pt.table, a.max_splits, a);
   return hipGetLastError();
 }
 

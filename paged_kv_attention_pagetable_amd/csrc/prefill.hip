@@ -182,14 +182,15 @@ struct SeqMeta {
 
 // Loaded once per workgroup, all four loads in flight together (start_pos,
 // when absent, re-reads cu_seqlens[n] and is replaced by 0).
-__device__ __forceinline__ SeqMeta seq_meta(const PrefillArgs& a, int n) {
+__device__ __forceinline__ SeqMeta seq_meta(const PrefillArgs& a, int n, const int32_t* cu_seqlens,
+                                            const int32_t* slots, const int32_t* start_pos) {
   SeqMeta m;
-  const int c0 = a.cu_seqlens[n], c1 = a.cu_seqlens[n + 1];
-  const int spv = (a.start_pos ? a.start_pos : a.cu_seqlens)[n];
-  const int slot = a.slots[n];
+  const int c0 = cu_seqlens[n], c1 = cu_seqlens[n + 1];
+  const int spv = (start_pos ? start_pos : cu_seqlens)[n];
+  const int slot = slots[n];
   m.a0 = __builtin_amdgcn_readfirstlane(c0);
   m.len = __builtin_amdgcn_readfirstlane(c1 - c0);
-  m.sp = a.start_pos ? __builtin_amdgcn_readfirstlane(spv) : 0;
+  m.sp = start_pos ? __builtin_amdgcn_readfirstlane(spv) : 0;
   m.slot = __builtin_amdgcn_readfirstlane(slot);
   const bool idle = m.slot <= 0 || m.slot >= a.pt.max_slots || m.sp < 0;
   const int kv_end = idle ? 0 : min(m.sp + m.len, a.pt.pps * a.g.page_size);
@@ -709,7 +710,11 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, const SeqMeta& sm
 template <int D, int NT, bool RQ>
 __global__ __launch_bounds__(prefill_threads<D>())
 __attribute__((amdgpu_waves_per_eu(prefill_wpe<D>(), prefill_wpe<D>())))
-void prefill_kernel(PrefillArgs a) {
+void prefill_kernel(const int32_t* cu_seqlens, const int32_t* slots, const int32_t* start_pos,
+                    const int32_t* table, int n_seqs, PrefillArgs a) {
+  // cu_seqlens .. n_seqs repeat fields of `a`: passed first, they arrive
+  // preloaded in scalar registers (the library builds this file with five
+  // preloaded kernel arguments), so the sequence metadata loads issue at once.
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int s_pg[kStagePages];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -717,12 +722,12 @@ void prefill_kernel(PrefillArgs a) {
   LaneConst<D> lc;
   lane_const<D>(lc, lane, w, a.g.page_size);
   const int hk = blockIdx.x, n = blockIdx.y;
-  if (n >= a.n_seqs) return;  // padding row of the grid (odd y extent)
-  const SeqMeta sm = seq_meta(a, n);
+  if (n >= n_seqs) return;  // padding row of the grid (odd y extent)
+  const SeqMeta sm = seq_meta(a, n, cu_seqlens, slots, start_pos);
   const int nblk = (sm.len + a.q_tokens - 1) / a.q_tokens;
   if (nblk <= a.n_qblocks - 1 - (int)blockIdx.z) return;  // no item in this layer
   {
-    const int32_t* trow = a.pt.table + (size_t)max(sm.slot, 0) * a.pt.pps;
+    const int32_t* trow = table + (size_t)max(sm.slot, 0) * a.pt.pps;
     for (int i = tid; i < sm.n_pg; i += prefill_threads<D>()) s_pg[i] = checked_page(trow[i], a.g.n_pages);
     __syncthreads();
   }
@@ -755,9 +760,11 @@ hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t st) {
   // the engines too but its per-workgroup set-up cost more than it saved.)
   dim3 grid(a.g.n_kv, a.n_seqs | 1, a.n_qblocks);
   if (a.q_w)
-    hipLaunchKernelGGL((prefill_kernel<D, NT, true>), grid, dim3(prefill_threads<D>()), lds, st, a);
+    hipLaunchKernelGGL((prefill_kernel<D, NT, true>), grid, dim3(prefill_threads<D>()), lds, st,
+                       a.cu_seqlens, a.slots, a.start_pos, a.pt.table, a.n_seqs, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, NT, false>), grid, dim3(prefill_threads<D>()), lds, st, a);
+    hipLaunchKernelGGL((prefill_kernel<D, NT, false>), grid, dim3(prefill_threads<D>()), lds, st,
+                       a.cu_seqlens, a.slots, a.start_pos, a.pt.table, a.n_seqs, a);
   return hipGetLastError();
 }
 
