@@ -32,14 +32,16 @@ COMMON = [
 
 
 # Per-source flags.  The decode kernels take their first four arguments
-# (slots, seq_lens, page table, split count) and the prefill kernel its first
-# five (cu_seqlens, slots, start_pos, page table, sequence count) ahead of
-# their argument structs, so that these arrive preloaded in scalar registers
-# and each workgroup's first loads (its row's or sequence's metadata) issue
+# (slots, seq_lens, page table, split count), the prefill kernel its first
+# five (cu_seqlens, slots, start_pos, page table, sequence count) and the
+# prologue kernel its first seven (the same metadata, the raw k and v rows,
+# the token count) ahead of their argument structs, so that these arrive
+# preloaded in scalar registers and each workgroup's first loads issue
 # without waiting for an argument load.
 PER_SOURCE = {
     "decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=4"],
     "prefill.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=5"],
+    "prologue.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=7"],
 }
 
 

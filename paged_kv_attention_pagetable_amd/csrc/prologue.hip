@@ -308,7 +308,22 @@ __device__ __forceinline__ void prologue_body(const PrologueArgs& a, ProSmem<D>&
 // grid = (nk_wg + n_kv, ceil(T / 64)): x < nk_wg takes k heads
 // pro_heads*x .., then one workgroup per v head.
 template <int D>
-__global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
+__global__ __launch_bounds__(256) void prologue_kernel(const int32_t* cu_seqlens, const int32_t* slots,
+                                                       const int32_t* start_pos, const bf16_t* k_raw,
+                                                       const bf16_t* v_raw, int T, int n_seqs,
+                                                       PrologueArgs args) {
+  // cu_seqlens .. n_seqs repeat fields of `args`: passed first, they arrive
+  // preloaded in scalar registers (the library builds this file with seven
+  // preloaded kernel arguments), so the first metadata and row loads issue
+  // at once.  (prologue_body is inlined: the copy stays in registers.)
+  PrologueArgs a = args;
+  a.cu_seqlens = cu_seqlens;
+  a.slots = slots;
+  a.start_pos = start_pos;
+  a.k_raw = k_raw;
+  a.v_raw = v_raw;
+  a.T = T;
+  a.n_seqs = n_seqs;
   __shared__ ProSmem<D> sm;
   const int nk_wg = (a.g.n_kv + pro_heads<D>() - 1) / pro_heads<D>();
   const int x = blockIdx.x;
@@ -328,7 +343,8 @@ hipError_t launch_prologue_d(const PrologueArgs& a, hipStream_t st) {
   // 256-byte pieces strided across many tokens.
   const int nk_wg = (a.g.n_kv + pro_heads<D>() - 1) / pro_heads<D>();
   dim3 grid(nk_wg + a.g.n_kv, (a.T + kProTokens - 1) / kProTokens);
-  hipLaunchKernelGGL((prologue_kernel<D>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prologue_kernel<D>), grid, dim3(256), 0, st, a.cu_seqlens, a.slots, a.start_pos,
+                     a.k_raw, a.v_raw, a.T, a.n_seqs, a);
   return hipGetLastError();
 }
 
