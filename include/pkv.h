@@ -238,7 +238,7 @@ pkv_status pkv_rope_table(float* cos_out, float* sin_out, int32_t max_pos,
                           int32_t head_dim, double theta, void* stream);
 
 /* pkv_rope_table_partial -- the same with only the leading rotary_fraction of
- * the head_dim/2 frequencies rotating: i < round(rotary_fraction * head_dim/2)
+ * the head_dim/2 frequencies rotating: i < floor(rotary_fraction * head_dim / 2)
  * use theta^(-2i/head_dim), the rest have a zero frequency (cos 1, sin 0), so
  * the prologue's full-head rotate_half passes those dims through.  This is
  * the "proportional" partial RoPE of the Gemma-4 full-attention layers

@@ -18,12 +18,17 @@ per-head q/k RMSNorm):
 
 Reading taken where the pages are silent: the frequencies are the "default"
 rope type's ``w_i = theta ** (-2 i / D)``, ``i = 0 .. D/2-1`` (the pages name
-the rope type and theta only).  This convention is pinned by closed forms and
-invariants in ``tests/test_oracle_prologue.py``, not by any value printed on
-the pages.
+the rope type and theta only, and hand both rope types to the transformers
+rotary-embedding classes).  ``tests/test_oracle_prologue.py`` pins this,
+and the partial ("proportional") variant below, against those library
+classes -- the default and proportional rope initialisers, the Qwen3 and
+Gemma-4 RMSNorm modules and ``apply_rotary_pos_emb`` -- besides closed forms
+and invariants.
 """
 
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -50,13 +55,16 @@ def rope_inv_freq_partial(head_dim: int, theta: float, rotary_fraction: float):
     the ``_apply_rotary_full`` docstring): only the leading
     ``rotary_fraction`` of the frequencies rotate; the tail entries of
     ``inv_freq`` are zero, so their cos = 1, sin = 0 and ``rotate_half`` over
-    the full head_dim passes those dims through.  Reading taken where the
-    pages are silent: the rotating frequencies keep the default exponents
-    over the full head_dim, ``theta ** (-2i / D)`` for
-    ``i < round(rotary_fraction * D / 2)``.
+    the full head_dim passes those dims through.  (The
+    ``_compute_rotary_per_layer_type`` docstring puts the same thing as the
+    initialiser slicing the head dim to ``rotary_fraction * head_dim``
+    rotating dims.)  Reading taken where the pages are silent: the rotating
+    frequencies keep the default exponents over the full head_dim,
+    ``theta ** (-2i / D)`` for ``i < floor(rotary_fraction * D / 2)`` -- the
+    count the library's proportional initialiser takes.
     """
     inv = rope_inv_freq(head_dim, theta)
-    n_rot = int(round(rotary_fraction * (head_dim // 2)))
+    n_rot = int(math.floor(rotary_fraction * head_dim / 2))
     inv[n_rot:] = 0.0
     return inv
 

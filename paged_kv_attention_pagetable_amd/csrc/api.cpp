@@ -414,7 +414,8 @@ pkv_status pkv_rope_table_partial(float* cos_out, float* sin_out, int32_t max_po
     return fail(PKV_ERR_INVALID_ARG, "%s: theta must be finite and > 0", fn);
   if (!(rotary_fraction > 0.0 && rotary_fraction <= 1.0))
     return fail(PKV_ERR_INVALID_ARG, "%s: rotary_fraction must be in (0, 1]", fn);
-  const int n_rot = (int)std::lround(rotary_fraction * (head_dim / 2));
+  // rotating frequencies: floor(f * D / 2), as the proportional rope initialiser counts them
+  const int n_rot = (int)std::floor(rotary_fraction * head_dim / 2.0);
   return launched(pkv::launch_rope_table(cos_out, sin_out, max_pos, head_dim, theta, n_rot,
                                          static_cast<hipStream_t>(stream)),
                   fn);

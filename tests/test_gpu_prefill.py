@@ -244,15 +244,20 @@ def test_mixed_prefill_and_decode_rows_with_prologue():
     _check_with_prologue(case, kp, vp, table, okp, ovp, "mixed with prologue")
 
 
-def test_rope_table_partial_matches_fp64():
-    D, theta, max_pos = 512, 1e6, 1024
-    c, s = pkv.rope_table(max_pos, D, theta, rotary_fraction=0.25)
+@pytest.mark.parametrize("D,fraction,n_rot", [(512, 0.25, 64), (64, 0.27, 8), (128, 0.3, 19),
+                                              (256, 0.1, 12)])
+def test_rope_table_partial_matches_fp64(D, fraction, n_rot):
+    """floor(f * D / 2) rotating frequencies (0.27 at D 64: 8, where rounding
+    would give 9), the rest cos 1 / sin 0."""
+    theta, max_pos = 1e6, 1024
+    c, s = pkv.rope_table(max_pos, D, theta, rotary_fraction=fraction)
     torch.cuda.synchronize()
-    inv = oracle.rope_inv_freq_partial(D, theta, 0.25)
+    inv = oracle.rope_inv_freq_partial(D, theta, fraction)
+    assert int((inv > 0).sum()) == n_rot
     ang = np.arange(max_pos)[:, None] * inv[None, :]
     assert np.max(np.abs(c.cpu().numpy() - np.cos(ang))) <= 1e-7
     assert np.max(np.abs(s.cpu().numpy() - np.sin(ang))) <= 1e-7
-    assert np.all(c.cpu().numpy()[:, 64:] == 1.0) and np.all(s.cpu().numpy()[:, 64:] == 0.0)
+    assert np.all(c.cpu().numpy()[:, n_rot:] == 1.0) and np.all(s.cpu().numpy()[:, n_rot:] == 0.0)
 
 
 # Gemma-4 prologue variants: sliding layers (head_dim 256, theta 1e4, window

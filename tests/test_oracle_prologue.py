@@ -1,9 +1,15 @@
 """Pins of the oracle's prologue (RMSNorm + half-split RoPE), CPU only.
 
 The pages fix the structure (RMSNorm over head_dim, then
-``x*cos + rotate_half(x)*sin``) but print no values; the frequency
-convention (``theta ** (-2i/D)``) is a reading, pinned here only by its own
-closed forms.
+``x*cos + rotate_half(x)*sin``) and name the rope types ("default" for the
+Qwen3 and Gemma-4 sliding layers, "proportional" with a partial rotary
+factor for the Gemma-4 full layers), which they take from the transformers
+rotary-embedding classes; they print no values.  Besides closed forms and
+invariants, the oracle's frequencies, norms and rotation are pinned here
+against that library's own implementation of those rope types (the
+default / proportional initialisers, ``Qwen3RMSNorm``, ``Gemma4RMSNorm``,
+the rotary-embedding modules and ``apply_rotary_pos_emb``): an independent
+implementation, so a wrong exponent, count, sign or half-split fails.
 """
 
 import math
@@ -123,7 +129,7 @@ def test_partial_rotary_frequencies_and_passthrough():
     rest (zero inv_freq) passes through; closed forms at D = 16."""
     D, theta = 16, 100.0
     inv = oracle.rope_inv_freq_partial(D, theta, 0.25)
-    # round(0.25 * 8) = 2 rotating frequencies: 1 and theta^(-2/16)
+    # floor(0.25 * 16 / 2) = 2 rotating frequencies: 1 and theta^(-2/16)
     assert inv[0] == 1.0 and abs(inv[1] - theta ** (-0.125)) <= 1e-15
     assert np.all(inv[2:] == 0.0)
     x = np.arange(1, D + 1, dtype=np.float64)
@@ -184,3 +190,140 @@ def test_gemma4_partial_rotary_keeps_tail_and_norm():
     assert np.max(np.abs(q2[..., tail] - qn[..., tail])) <= 1e-15
     # a rotation keeps each row's norm
     assert np.max(np.abs(np.linalg.norm(q2, axis=-1) - np.linalg.norm(qn, axis=-1))) <= 1e-12
+
+
+# ------------------------------------------- pins against transformers ----
+# The library computes its tables in float32, so agreement is to float32
+# rounding: frequencies to a few ulp, rotated values to ~1e-4 at positions
+# up to ~1000 (the fp32 angle pos * inv_freq).  A wrong convention
+# (exponent, rotating count, half order, sign) is off by O(1).
+
+def _qwen3_config(head_dim, theta, rope_type="default", fraction=None):
+    transformers = pytest.importorskip("transformers")
+    rp = {"rope_type": rope_type, "rope_theta": theta}
+    if fraction is not None:
+        rp["partial_rotary_factor"] = fraction
+    return transformers.Qwen3Config(head_dim=head_dim, hidden_size=8 * head_dim,
+                                    num_attention_heads=8, num_key_value_heads=2,
+                                    rope_parameters=rp)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
+@pytest.mark.parametrize("theta", [1e4, 1e6])
+def test_default_rope_frequencies_match_transformers(D, theta):
+    pytest.importorskip("transformers")
+    from transformers.models.qwen3.modeling_qwen3 import Qwen3RotaryEmbedding
+    inv, scaling = Qwen3RotaryEmbedding.compute_default_rope_parameters(_qwen3_config(D, theta))
+    assert scaling == 1.0
+    ref = inv.double().numpy()
+    got = oracle.rope_inv_freq(D, theta)
+    assert got.shape == ref.shape
+    assert np.max(np.abs(got - ref) / ref) <= 4e-7
+
+
+@pytest.mark.parametrize("D,fraction", [(512, 0.25), (64, 0.27), (64, 0.5), (128, 0.3),
+                                        (256, 0.1), (96, 0.75), (512, 1.0)])
+def test_proportional_rope_frequencies_match_transformers(D, fraction):
+    """Rotating count floor(f * D / 2), default exponents over the full head_dim,
+    zero tail: the library's proportional initialiser.  (0.27 at D 64 is a case
+    where rounding would give 9 rotating frequencies and the library gives 8.)"""
+    pytest.importorskip("transformers")
+    from transformers.modeling_rope_utils import ROPE_INIT_FUNCTIONS
+    cfg = _qwen3_config(D, 1e6, "proportional", fraction)
+    inv, _ = ROPE_INIT_FUNCTIONS["proportional"](cfg, None)
+    ref = inv.double().numpy()
+    got = oracle.rope_inv_freq_partial(D, 1e6, fraction)
+    assert got.shape == ref.shape
+    assert np.array_equal(got == 0.0, ref == 0.0), "rotating count differs"
+    nz = ref > 0
+    assert np.max(np.abs(got[nz] - ref[nz]) / ref[nz]) <= 4e-7
+
+
+def test_gemma4_layer_rope_tables_match_transformers():
+    """The Gemma-4 text config's own two rope types (sliding: default, theta 10K,
+    head_dim 256; full: proportional 0.25, theta 1M, head_dim 512)."""
+    pytest.importorskip("transformers")
+    from transformers.models.gemma4 import configuration_gemma4, modeling_gemma4
+    cfg = configuration_gemma4.Gemma4TextConfig()
+    rot = modeling_gemma4.Gemma4TextRotaryEmbedding(cfg)
+    for lt, D, theta, frac in (("sliding_attention", 256, 1e4, 1.0),
+                               ("full_attention", 512, 1e6, 0.25)):
+        assert cfg.per_layer_config[lt].head_dim == D
+        ref = getattr(rot, f"{lt}_inv_freq").double().numpy()
+        got = oracle.rope_inv_freq_partial(D, theta, frac)
+        assert np.array_equal(got == 0.0, ref == 0.0)
+        nz = ref > 0
+        assert np.max(np.abs(got[nz] - ref[nz]) / ref[nz]) <= 4e-7
+
+
+def _rows(D, seed, n=6, pos_hi=1024):
+    rng = np.random.default_rng(seed)
+    from synth import randn_bf16
+    x = randn_bf16(rng, (n, 3, D))          # [tokens][heads][D] bf16 bits
+    w = randn_bf16(rng, (D,), 1.0, 0.1)
+    pos = rng.integers(0, pos_hi, size=n).astype(np.int64)
+    pos[0] = 0
+    return x, w, pos
+
+
+def test_qwen3_prologue_matches_transformers():
+    """q' = rope(RMSNorm(q) * w) via Qwen3RMSNorm, Qwen3RotaryEmbedding and
+    apply_rotary_pos_emb (fp32 inputs, so the module's cast back to the input
+    dtype rounds nothing) against oracle.prologue_qwen3."""
+    torch = pytest.importorskip("torch")
+    pytest.importorskip("transformers")
+    from transformers.models.qwen3 import modeling_qwen3 as mq
+    D, theta, eps = 128, 1e6, 1e-6
+    x, w, pos = _rows(D, 31)
+    q2, k2, _ = oracle.prologue_qwen3(x, x[:, :2], x[:, :2], w, w, pos, eps, theta)
+    xf = torch.from_numpy(oracle.bf16_bits_to_f64(x)).float()      # [T][H][D]
+    norm = mq.Qwen3RMSNorm(D, eps=eps)
+    with torch.no_grad():
+        norm.weight.copy_(torch.from_numpy(oracle.bf16_bits_to_f64(w)).float())
+        rot = mq.Qwen3RotaryEmbedding(_qwen3_config(D, theta))
+        cos, sin = rot(xf, torch.from_numpy(pos)[None])             # [1][T][D]
+        xn = norm(xf).double()
+        ref, _ = mq.apply_rotary_pos_emb(xn[None].transpose(1, 2), xn[None].transpose(1, 2),
+                                         cos.double(), sin.double(), unsqueeze_dim=1)
+    ref = ref[0].transpose(0, 1).numpy()                           # [T][H][D]
+    assert np.max(np.abs(q2 - ref)) <= 5e-4
+    assert np.max(np.abs(k2 - ref[:, :2])) <= 5e-4
+    # position 0 involves no angle: there the agreement is to fp32 norm rounding
+    assert np.max(np.abs(q2[0] - ref[0])) <= 2e-6
+
+
+@pytest.mark.parametrize("layer", ["sliding_attention", "full_attention"])
+def test_gemma4_prologue_matches_transformers(layer):
+    """Gemma-4 layers through the library's Gemma4RMSNorm (q_norm / k_norm with
+    a gain, v_norm without), its per-layer-type rotary embedding and
+    apply_rotary_pos_emb; full layers with K = V (value = v_norm of the raw
+    k projection) and the partial rotary."""
+    torch = pytest.importorskip("torch")
+    pytest.importorskip("transformers")
+    from transformers.models.gemma4 import configuration_gemma4, modeling_gemma4 as mg
+    cfg = configuration_gemma4.Gemma4TextConfig()
+    full = layer == "full_attention"
+    D = cfg.per_layer_config[layer].head_dim
+    theta, frac = (1e6, 0.25) if full else (1e4, 1.0)
+    eps = 1e-6
+    x, w, pos = _rows(D, 37 if full else 41)
+    kraw = x[:, :2]
+    vraw = x[:, 1:3]
+    q2, k2, v2 = oracle.prologue_gemma4(x, kraw, vraw, w, w, pos, eps, theta,
+                                        rotary_fraction=frac, k_eq_v=full)
+    rot = mg.Gemma4TextRotaryEmbedding(cfg)
+    xf = torch.from_numpy(oracle.bf16_bits_to_f64(x)).float()
+    with torch.no_grad():
+        norm = mg.Gemma4RMSNorm(D, eps=eps)
+        norm.weight.copy_(torch.from_numpy(oracle.bf16_bits_to_f64(w)).float())
+        vnorm = mg.Gemma4RMSNorm(D, eps=eps, with_scale=False)
+        cos, sin = rot(xf, torch.from_numpy(pos)[None], layer)
+        xn = norm(xf).double()[None]                                 # [1][T][H][D]
+        # the attention forward's call: (batch, seq, heads, head_dim), unsqueeze at 2
+        ref = mg.apply_rotary_pos_emb(xn, cos.double(), sin.double(), unsqueeze_dim=2)
+        vsrc = xf[:, :2] if full else xf[:, 1:3]
+        vref = vnorm(vsrc).double().numpy()
+    ref = ref[0].numpy()
+    assert np.max(np.abs(q2 - ref)) <= 5e-4
+    assert np.max(np.abs(k2 - ref[:, :2])) <= 5e-4
+    assert np.max(np.abs(v2 - vref)) <= 2e-6
