@@ -1,20 +1,25 @@
 #!/usr/bin/env python3
 """Throughput bench of the paged KV-cache attention path on one MI355X.
 
-Default workload (``qwen3_decode``): a Qwen3-4B-shaped decode step -- 8 active
-slots of 9 (slot 0 reserved), 32 query / 8 kv heads, head_dim 128, page 128,
-context lengths U[64, 1024], 36 layers each with its own K/V pools.  One step
-= for every layer: append the new token's K/V into the pages, then split-K
-decode attention (+ log-sum-exp merge).  A second timed phase runs the
-Qwen3-4B-shaped chunked prefill (16 prompts U[32, 512], fused q/k RMSNorm +
-RoPE + append prologue, then MFMA prefill attention, 36 layers) and is
-reported under ``prefill``.
+Default workload (``llama_decode``): a Llama-3.2-3B-shaped decode step -- 64
+slots (10 % idle, length 0), 24 query / 8 kv heads, head_dim 128, page 128,
+context lengths U[128, 4096], two layers with their own K/V pools (together
+above the 256 MB Infinity Cache).  One step = for every layer: the split-K
+decode kernel, which appends each row's new token's K/V into its page and
+then attends (+ the in-kernel log-sum-exp merge).  This is the largest
+single-GPU decode configuration; it gives the JSON line's ``value`` and
+``roofline``.  The other decode workloads -- ``qwen3_decode`` (8 rows of a
+Qwen3-4B step, 36 layers) and ``gemma_mixed`` (64 rows, one Gemma-4 sliding
+head_dim-256 and one full head_dim-512 layer per step) -- are reported under
+``extra_decode`` with their own rooflines, and the Qwen3-4B chunked prefill
+(16 prompts U[32, 512], fused q/k RMSNorm + RoPE + append prologue, then MFMA
+prefill attention, 36 layers) under ``prefill``.
 
-Both phases are captured once in a HIP graph (through torch.cuda.CUDAGraph) and
+Every phase is captured once in a HIP graph (through torch.cuda.CUDAGraph) and
 replayed: inputs are resident in HBM before the timed region, and the timed
-region is bracketed by torch.cuda.synchronize().  Kernel-level durations for
-the roofline come from HIP events around graphs that hold only the attention
-calls, on the stream the kernels run on.
+region is bracketed by torch.cuda.synchronize().  Kernel durations for the
+rooflines come from HIP events around graphs of back-to-back calls of one
+kernel, recorded on the stream the kernels run on.
 
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: this path runs on one GPU.
 """
@@ -133,6 +138,12 @@ class DecodeWorkload:
         for ly in self.layers:
             self.attn(ly)
 
+    def step_kind(self, D):
+        """The step's calls of one head_dim only (per-layer-kind timing)."""
+        for ly in self.layers:
+            if ly["D"] == D:
+                self.attn(ly, fused_append=True)
+
     def attn_bytes(self, ly):
         """Algorithmic HBM bytes of one attention call: visible K/V rows, Q, O, page ids."""
         c, case = self.c, self.case
@@ -209,6 +220,13 @@ class PrefillWorkload:
                               scale=self.scale, start_pos=self.start,
                               max_seqlen_q_hint=self.c["len_hi"], prologue=pro, out=ly["out"])
 
+    def _call_q_only(self, ly):
+        """Attention with the fused q norm + RoPE, keys already in the pages."""
+        pro = dict(q_norm_w=ly["qw"], eps=self.c["eps"], cos=self.cos, sin=self.sin)
+        self.pkv.attn_prefill(ly["q"], self.cu, self.slots, self.table, ly["kp"], ly["vp"],
+                              scale=self.scale, start_pos=self.start,
+                              max_seqlen_q_hint=self.c["len_hi"], prologue=pro, out=ly["out"])
+
     def step(self):
         for ly in self.layers:
             self._call(ly, True)
@@ -216,6 +234,10 @@ class PrefillWorkload:
     def attn_only(self):
         for ly in self.layers:
             self._call(ly, False)
+
+    def attn_fused_q(self):
+        for ly in self.layers:
+            self._call_q_only(ly)
 
     def flops_per_call(self):
         """Causal attention FLOPs: 2 (QK^T) + 2 (PV) per visible (query, key) pair."""
@@ -376,14 +398,14 @@ def source_sha(names):
     return h.hexdigest()[:16]
 
 
-def pmc_traffic(tag, sources, launches_per_call=1):
+def pmc_traffic(part):
     """HBM bytes per call from a committed rocprofv3 PMC summary, if current."""
-    path = os.path.join(PROFILES, f"{tag}_pmc.json")
+    path = os.path.join(PROFILES, f"{part}_pmc.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha") != source_sha(sources):
+    if rec.get("source_sha") != source_sha(PMC_PARTS[part][1]):
         return None   # kernel changed since the counters were taken
     return rec.get("hbm_bytes_per_call")
 
@@ -429,21 +451,29 @@ def _pmc_per_kernel(db_path, counter):
     return acc
 
 
+DECODE_SRC = ["decode.hip", "pkv_device.h", "pkv_internal.h"]
+PREFILL_SRC = ["prefill.hip", "pkv_device.h", "pkv_internal.h"]
 PMC_PARTS = {
-    # part: (substrings a counted kernel's name contains, sources whose hash the
-    # record keeps).  Prefill counts the attention kernel without the fused q
-    # prologue: the instance the roofline times.
-    "decode": (("decode_",), ["decode.hip", "pkv_device.h", "pkv_internal.h"]),
-    "prefill": (("prefill_kernel<", ", false>"), ["prefill.hip", "pkv_device.h", "pkv_internal.h"]),
+    # part: (substrings a counted kernel instance's name contains, sources whose
+    # hash the record keeps).  The three decode workloads run distinct
+    # instances (Llama: 4-wave key split; Qwen3: 8-wave key split; Gemma: the
+    # head_dim-256 and -512 dim-split kernels, one call of each per step).
+    "decode_llama_decode": (("decode_keysplit_kernel<128, 4>",), DECODE_SRC),
+    "decode_qwen3_decode": (("decode_keysplit_kernel<128, 8>",), DECODE_SRC),
+    "decode_gemma_mixed": (("decode_dimsplit_kernel<",), DECODE_SRC),
+    # prefill attention without the q transform (keys appended beforehand)
+    "prefill_qwen3_prefill": (("prefill_kernel<", ", false>"), PREFILL_SRC),
+    # prefill attention with the fused q norm + RoPE
+    "prefill_fused_q_qwen3_prefill": (("prefill_kernel<", ", true>"), PREFILL_SRC),
 }
 
 
-def summarize_pmc(fetch_db, write_db, out_prefix, workload="qwen3_decode", command="",
-                  part="decode"):
-    """HBM bytes per call of the part's attention kernel = FETCH_SIZE + WRITE_SIZE
-    (KiB per dispatch), each scaled by what the counter reads for a 256 MiB device
-    copy.  Other library kernels of the run are listed for reference."""
-    key, sources = PMC_PARTS[part]
+def summarize_pmc(fetch_db, write_db, out_dir, command=""):
+    """HBM bytes per call of every part's kernel(s) = FETCH_SIZE + WRITE_SIZE (KiB
+    per dispatch), each scaled by what the counter reads for a 256 MiB device
+    copy (``--calibrate-copy``): one ``<part>_pmc.json`` per part whose kernels
+    ran.  Per call = the counted dispatches' bytes over their number.  Other
+    library kernels of the run are listed for reference."""
     fetch = _pmc_per_kernel(fetch_db, "FETCH_SIZE")
     write = _pmc_per_kernel(write_db, "WRITE_SIZE")
     copy_bytes = 128 * 2**20 * 2
@@ -453,26 +483,31 @@ def summarize_pmc(fetch_db, write_db, out_prefix, workload="qwen3_decode", comma
         return copy_bytes / (max(vals) * 1024.0) if vals else None
 
     f_scale, w_scale = copy_scale(fetch), copy_scale(write)
-    per_call = 0.0
-    parts = {}
-    for k in sorted(set(fetch) | set(write)):
-        if "pkv::" not in k:
+    for part, (key, sources) in PMC_PARTS.items():
+        total, n = 0.0, 0
+        parts = {}
+        for k in sorted(set(fetch) | set(write)):
+            if "pkv::" not in k:
+                continue
+            fv, wv = fetch.get(k, []), write.get(k, [])
+            fb = float(np.mean(fv or [0.0])) * 1024.0 * (f_scale or 1.0)
+            wb = float(np.mean(wv or [0.0])) * 1024.0 * (w_scale or 1.0)
+            counted = all(part_key in k for part_key in key)
+            if counted:
+                total += (fb + wb) * len(fv)
+                n += len(fv)
+            short = k.replace("void ", "").replace("pkv::(anonymous namespace)::", "").split("(")[0]
+            parts[short] = dict(fetch_bytes=round(fb), write_bytes=round(wb),
+                                dispatches=len(fv), counted=counted)
+        if n == 0:
             continue
-        fb = float(np.mean(fetch.get(k, [0.0]))) * 1024.0 * (f_scale or 1.0)
-        wb = float(np.mean(write.get(k, [0.0]))) * 1024.0 * (w_scale or 1.0)
-        counted = all(part_key in k for part_key in key)
-        if counted:
-            per_call += fb + wb
-        short = k.replace("void ", "").replace("pkv::(anonymous namespace)::", "").split("(")[0]
-        parts[short] = dict(fetch_bytes=round(fb), write_bytes=round(wb),
-                            dispatches=len(fetch.get(k, [])), counted=counted)
-    rec = dict(workload=workload, part=part, source_sha=source_sha(sources),
-               hbm_bytes_per_call=round(per_call), kernels=parts,
-               copy_scale=dict(fetch=f_scale, write=w_scale, copy_bytes=copy_bytes),
-               command=command)
-    with open(out_prefix + ".json", "w") as f:
-        json.dump(rec, f, indent=1)
-    print(json.dumps(rec))
+        rec = dict(part=part, source_sha=source_sha(sources), hbm_bytes_per_call=round(total / n),
+                   kernels=parts, copy_scale=dict(fetch=f_scale, write=w_scale,
+                                                  copy_bytes=copy_bytes),
+                   command=command)
+        with open(os.path.join(out_dir, f"{part}_pmc.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(dict(part=part, hbm_bytes_per_call=rec["hbm_bytes_per_call"])))
 
 
 MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_WAVES",
@@ -507,7 +542,7 @@ def summarize_mfma(db_path, out_path, command=""):
     gui = vals.get("GRBM_GUI_ACTIVE")
     busy = vals.get("SQ_VALU_MFMA_BUSY_CYCLES")
     rec = dict(kernel="prefill_kernel<128, 2, false> (qwen3_prefill attention)",
-               source_sha=source_sha(PMC_PARTS["prefill"][1]), counters=vals,
+               source_sha=source_sha(PREFILL_SRC), counters=vals,
                kernel_ns_under_counters=dur_ns, command=command)
     if gui and busy:
         rec["mfma_busy_fraction"] = round(busy / (gui / N_XCD * N_CU * 4), 4)
@@ -525,23 +560,42 @@ def summarize_mfma(db_path, out_path, command=""):
 # CPU oracle baseline (bounded sample)
 # ----------------------------------------------------------------------------
 
-def cpu_decode_baseline(seconds):
+CPU_SAMPLE_ROWS = 8   # rows of the decode workload one oracle sample call covers
+
+
+def _cpu_decode_sample(name):
+    """The first CPU_SAMPLE_ROWS rows of a decode workload (same lengths,
+    slots, heads and pages as the GPU run), pools holding the history, and the
+    algorithmic bytes of one fused call on them (append of the new token +
+    attention, counted as on the GPU)."""
     import oracle
     from synth import CONFIGS, config_lengths, make_decode_case
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    c = CONFIGS["qwen3_decode"]
-    lengths, slots = config_lengths("qwen3_decode")
-    case = make_decode_case(c["n_q"], c["n_kv"], c["head_dim"], c["page_size"], lengths,
+    c = CONFIGS[name]
+    lengths, slots = config_lengths(name)
+    lengths, slots = lengths[:CPU_SAMPLE_ROWS], slots[:CPU_SAMPLE_ROWS]
+    D = c.get("head_dim", c.get("full_dim"))
+    case = make_decode_case(c["n_q"], c["n_kv"], D, c["page_size"], lengths,
                             max_slots=c["max_slots"], seed=3407 + c["index"], slot_of_row=slots,
                             pages_per_slot=-(-c["len_hi"] // c["page_size"]))
     kp, vp = case.empty_pools()
     hk, hv, hs, hp = case.history_tokens()
     oracle.append(kp, vp, case.table, hk, hv, hs, hp)
-    per_call = (int(case.seq_lens.sum()) * c["n_kv"] * c["head_dim"] * 4
-                + case.B * c["n_q"] * c["head_dim"] * 4)
+    L = case.seq_lens.astype(np.int64)
+    active = int((L > 0).sum())
+    per_call = (int(L.sum()) * c["n_kv"] * D * 4 + active * c["n_q"] * D * 4
+                + int(np.ceil(L / case.page_size).sum()) * 4
+                + active * c["n_kv"] * D * 2 * 4)
+    return case, kp, vp, per_call
+
+
+def _cpu_decode_run(name, seconds):
+    """One process, one BLAS thread: fused oracle calls for ~`seconds`."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    case, kp, vp, per_call = _cpu_decode_sample(name)
     ctx = threadpool_limits(1) if threadpool_limits else None
     if ctx:
         ctx.__enter__()
@@ -559,13 +613,38 @@ def cpu_decode_baseline(seconds):
     finally:
         if ctx:
             ctx.__exit__(None, None, None)
-    return dict(value=round(n * per_call / el / 1e9, 6), unit="GB/s", cores=1, kind="oracle",
-                sample=f"{n} qwen3_decode layer calls (8 rows, append + attention, "
-                       f"fp64 numpy, 1 BLAS thread) in {el:.1f} s",
+    return n, n * per_call, el
+
+
+def cpu_decode_baseline(name, seconds, processes=1):
+    """The fp64 oracle on a bounded sample of the decode workload, scaled to
+    GB/s of the same algorithmic bytes as the GPU line.  processes > 1: that
+    many concurrent oracle processes (one BLAS thread each, started fresh,
+    never forked from this GPU process), aggregate bytes over the longest
+    one's time."""
+    if processes <= 1:
+        n, nbytes, el = _cpu_decode_run(name, seconds)
+        calls, cores = n, 1
+    else:
+        import multiprocessing as mp
+        with mp.get_context("spawn").Pool(processes) as pool:
+            res = pool.starmap(_cpu_decode_run, [(name, seconds)] * processes)
+        calls = sum(r[0] for r in res)
+        nbytes = sum(r[1] for r in res)
+        el = max(r[2] for r in res)
+        cores = processes
+    return dict(value=round(nbytes / el / 1e9, 6), unit="GB/s", cores=cores, kind="oracle",
+                sample=f"{calls} {name} fused calls (append + attention) on the workload's "
+                       f"first {CPU_SAMPLE_ROWS} rows, fp64 numpy, "
+                       + ("1 BLAS thread" if cores == 1 else
+                          f"{cores} concurrent processes of 1 BLAS thread each")
+                       + f", in {el:.1f} s",
                 seconds=round(el, 2))
 
 
-def cpu_prefill_baseline(seconds):
+def _cpu_prefill_run(seconds):
+    """One process, one BLAS thread: the prefill oracle (prologue and append of
+    every token, then attention token by token) until `seconds` pass."""
     import oracle
     from synth import CONFIGS, config_lengths, make_prefill_case
     try:
@@ -604,41 +683,166 @@ def cpu_prefill_baseline(seconds):
     finally:
         if ctx:
             ctx.__exit__(None, None, None)
-    return dict(value=round(flops / el / 1e12, 9), unit="TFLOP/s", cores=1, kind="oracle",
-                sample=f"prologue + append of all {case.T} tokens, then attention of the first "
-                       f"{done} query tokens (fp64 numpy, 1 BLAS thread) in {el:.1f} s",
+    return flops, el, done, case.T
+
+
+def cpu_prefill_baseline(seconds, processes=1):
+    if processes <= 1:
+        flops, el, done, T = _cpu_prefill_run(seconds)
+        cores = 1
+    else:
+        import multiprocessing as mp
+        with mp.get_context("spawn").Pool(processes) as pool:
+            res = pool.map(_cpu_prefill_run, [seconds] * processes)
+        flops = sum(r[0] for r in res)
+        el = max(r[1] for r in res)
+        done = sum(r[2] for r in res)
+        T = res[0][3]
+        cores = processes
+    return dict(value=round(flops / el / 1e12, 9), unit="TFLOP/s", cores=cores, kind="oracle",
+                sample=f"prologue + append of all {T} tokens, then attention of "
+                       + (f"the first {done} query tokens (fp64 numpy, 1 BLAS thread)"
+                          if cores == 1 else
+                          f"{done} query tokens in all ({cores} concurrent processes of 1 BLAS "
+                          "thread, each running the whole sample)")
+                       + f" in {el:.1f} s",
                 seconds=round(el, 2))
 
 
 # ----------------------------------------------------------------------------
+
+def decode_record(name, args, headline=False):
+    """Time one decode workload's step (every layer: the fused append +
+    attention kernel) and its kernel; returns the record for the JSON line."""
+    import torch
+    log(f"setting up {name}")
+    wl = DecodeWorkload(name, contiguous=args.contiguous_pages)
+    g_step = capture(wl.step)
+    log(f"timing {name}")
+    torch.cuda.synchronize()
+    ms_step = time_graph(g_step, args.steps, args.warmup)
+    each = time_graph_each(g_step, args.steps)
+    # kernel time per call: the same graph replayed back to back (HIP events on
+    # the graph's stream); every dispatch of the step is one decode kernel
+    ms_call = time_graph(g_step, args.kernel_reps, 2) / wl.n_calls
+    call_bytes = [wl.attn_bytes(ly) + wl.append_bytes(ly) for ly in wl.layers]
+    step_bytes = sum(call_bytes)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = (step_bytes / wl.n_calls) / (ms_call * 1e-3) / 1e9
+    traffic = None if args.contiguous_pages else pmc_traffic(f"decode_{name}")
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                    kernel="decode (split-K kernel: fused append of the new token, attention, "
+                           "last split merges)",
+                    algorithmic_bytes_per_call=int(step_bytes / wl.n_calls),
+                    us_per_call=round(ms_call * 1e3, 3))
+    rec = dict(config=wl.describe(), ms_per_step=round(ms_step, 4), value=round(value, 1),
+               unit="GB/s", roofline=roofline,
+               step_ms_median=round(float(np.median(each)), 4), step_ms_best=round(min(each), 4))
+    dims = sorted({ly["D"] for ly in wl.layers})
+    if len(dims) > 1:
+        # per layer kind (Gemma: the sliding head_dim-256 and full head_dim-512 calls)
+        rec["per_kind"] = {}
+        for D in dims:
+            g = capture(lambda D=D: wl.step_kind(D))
+            lys = [ly for ly in wl.layers if ly["D"] == D]
+            ms = time_graph(g, args.kernel_reps, 2) / len(lys)
+            b = sum(wl.attn_bytes(ly) + wl.append_bytes(ly) for ly in lys) / len(lys)
+            rec["per_kind"][f"head_dim_{D}"] = dict(
+                us_per_call=round(ms * 1e3, 3), algorithmic_bytes_per_call=int(b),
+                achieved=round(b / (ms * 1e-3) / 1e9, 1),
+                frac=round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                window=max(ly["window"] for ly in lys))
+            del g
+    if args.attn_only:
+        g_attn = capture(wl.attn_only)
+        ms_a = time_graph(g_attn, args.kernel_reps, 2) / wl.n_calls
+        ab = sum(wl.attn_bytes(ly) for ly in wl.layers) / wl.n_calls
+        rec["attn_only"] = dict(us_per_call=round(ms_a * 1e3, 3),
+                                achieved=round(ab / (ms_a * 1e-3) / 1e9, 1))
+        del g_attn
+    if headline:
+        rec["device_reserve"] = reserve_timing(wl)
+    del g_step, wl
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def prefill_record(args):
+    import torch
+    log("setting up qwen3_prefill")
+    pw = PrefillWorkload(contiguous=args.contiguous_pages)
+    gp_step = capture(pw.step)
+    gp_attn = capture(pw.attn_only)
+    gp_fq = capture(pw.attn_fused_q)
+    log("timing prefill")
+    ms_p = time_graph(gp_step, args.steps, args.warmup)
+    each_p = time_graph_each(gp_step, args.steps)
+    ms_pa = time_graph(gp_attn, args.kernel_reps, 2) / pw.n_calls
+    ms_fq = time_graph(gp_fq, args.kernel_reps, 2) / pw.n_calls
+    fl = pw.flops_per_call()
+
+    def roof(ms, part, kernel):
+        tf = fl / (ms * 1e-3) / 1e12
+        return dict(bound="mfma", achieved=round(tf, 2), peak=MFMA_BF16_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                    traffic=None if args.contiguous_pages else pmc_traffic(part),
+                    kernel=kernel, algorithmic_flops_per_call=fl,
+                    us_per_call=round(ms * 1e3, 3))
+
+    rec = {
+        "config": pw.describe(), "ms_per_step": round(ms_p, 4),
+        "step_ms_median": round(float(np.median(each_p)), 4),
+        "step_ms_best": round(min(each_p), 4),
+        # a whole layer: k/v prologue kernel + attention with the fused q transform
+        "tflops_step": round(fl * pw.n_calls / (ms_p * 1e-3) / 1e12, 2),
+        "roofline": roof(ms_pa, "prefill_qwen3_prefill",
+                         "prefill attention (keys already in the pages, q as given)"),
+        "roofline_fused_q": roof(ms_fq, "prefill_fused_q_qwen3_prefill",
+                                 "prefill attention with the fused q RMSNorm + RoPE (the "
+                                 "instance a prefill layer with the prologue runs)"),
+        "prologue_us_per_call": round((ms_p / pw.n_calls - ms_fq) * 1e3, 3),
+        "prologue_bytes_per_call": pw.prologue_bytes(),
+    }
+    del gp_step, gp_attn, gp_fq, pw
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_decode",
-                    choices=["qwen3_decode", "llama_decode", "gemma_mixed"])
+    ap.add_argument("--workload", default="llama_decode",
+                    choices=["llama_decode", "qwen3_decode", "gemma_mixed"],
+                    help="the decode workload of the headline line (default: the largest)")
+    ap.add_argument("--no-extra-decode", action="store_true",
+                    help="skip the other decode workloads")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--attn-only", action="store_true",
+                    help="also time decode attention without the fused append")
     ap.add_argument("--contiguous-pages", action="store_true",
                     help="map each slot's pages to consecutive physical pages instead of a "
                          "random permutation (times the page indirection)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
+    ap.add_argument("--cpu-processes", type=int, default=0,
+                    help="processes of the all-cores CPU leg (0: the host's cores, at most 16)")
     ap.add_argument("--kernel-reps", type=int, default=20,
-                    help="replays of the attention-only graphs for kernel timing")
+                    help="replays of the graphs timed for kernel durations")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DB", "OUT"),
                     help="write a kernel-duration summary of a rocprofv3 database and exit")
-    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "OUT"),
-                    help="write HBM traffic per attention call from two rocprofv3 --pmc "
-                         "runs (FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "OUT_DIR"),
+                    help="write HBM traffic per call of every part's kernels from two "
+                         "rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) and exit")
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("DB", "OUT"),
                     help="write the prefill kernel's matrix-core counters from one rocprofv3 "
                          "--pmc run and exit")
-    ap.add_argument("--pmc-part", default="decode", choices=sorted(PMC_PARTS),
-                    help="which attention kernel --summarize-pmc counts per call")
     ap.add_argument("--command", default="", help="command line recorded in summaries")
     args = ap.parse_args()
     if args.summarize_trace:
@@ -648,8 +852,7 @@ def main():
         summarize_mfma(*args.summarize_mfma, command=args.command)
         return
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc, workload=args.workload, command=args.command,
-                      part=args.pmc_part)
+        summarize_pmc(*args.summarize_pmc, command=args.command)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this bench runs the single-GPU path only; "
@@ -664,38 +867,25 @@ def main():
     import paged_kv_attention_pagetable_amd as pkv
     pkv.lib()
 
-    log(f"setting up {args.workload}")
-    wl = DecodeWorkload(args.workload, contiguous=args.contiguous_pages)
-    g_step = capture(wl.step)
-    g_attn = capture(wl.attn_only)
-    log("timing decode step")
-    torch.cuda.synchronize()
-    ms_step = time_graph(g_step, args.steps, args.warmup)
-    each = time_graph_each(g_step, args.steps)
-    ms_attn = time_graph(g_attn, args.kernel_reps, 2) / wl.n_calls
-    attn_bytes = [wl.attn_bytes(ly) for ly in wl.layers]
-    step_bytes = sum(attn_bytes) + sum(wl.append_bytes(ly) for ly in wl.layers)
-    value = step_bytes / (ms_step * 1e-3) / 1e9
-    achieved = (sum(attn_bytes) / wl.n_calls) / (ms_attn * 1e-3) / 1e9
-    traffic = pmc_traffic(f"decode_{args.workload}", PMC_PARTS["decode"][1])
-    if args.contiguous_pages:
-        traffic = None   # the committed counters were taken on permuted tables
-    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-                    kernel="decode attention (split-K kernel, last split merges)",
-                    algorithmic_bytes_per_call=int(sum(attn_bytes) / wl.n_calls),
-                    us_per_call=round(ms_attn * 1e3, 3))
+    head = decode_record(args.workload, args, headline=True)
     result = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "metric": METRIC, "value": head["value"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16, "
                 + ("contiguous pages)" if args.contiguous_pages else "random page permutation)"),
-        "config": wl.describe(), "roofline": roofline,
-        "step_ms_median": round(float(np.median(each)), 4), "step_ms_best": round(min(each), 4),
+        "config": head["config"], "roofline": head["roofline"],
+        "step_ms_median": head["step_ms_median"], "step_ms_best": head["step_ms_best"],
+        "device_reserve": head["device_reserve"],
     }
-    del g_step, g_attn
-    result["device_reserve"] = reserve_timing(wl)
+    for k in ("attn_only", "per_kind"):
+        if k in head:
+            result[k] = head[k]
+    if not args.no_extra_decode:
+        result["extra_decode"] = {}
+        for name in ("qwen3_decode", "llama_decode", "gemma_mixed"):
+            if name != args.workload:
+                result["extra_decode"][name] = decode_record(name, args)
     if args.calibrate_copy:
         src = torch.empty(128 * 2**20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -703,39 +893,20 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-
     if not args.no_prefill:
-        log("setting up qwen3_prefill")
-        pw = PrefillWorkload(contiguous=args.contiguous_pages)
-        gp_step = capture(pw.step)
-        gp_attn = capture(pw.attn_only)
-        log("timing prefill")
-        ms_p = time_graph(gp_step, args.steps, args.warmup)
-        each_p = time_graph_each(gp_step, args.steps)
-        ms_pa = time_graph(gp_attn, args.kernel_reps, 2) / pw.n_calls
-        fl = pw.flops_per_call()
-        tflops = fl / (ms_pa * 1e-3) / 1e12
-        result["prefill"] = {
-            "config": pw.describe(), "ms_per_step": round(ms_p, 4),
-            "step_ms_median": round(float(np.median(each_p)), 4),
-            "step_ms_best": round(min(each_p), 4),
-            "tflops_step": round(fl * pw.n_calls / (ms_p * 1e-3) / 1e12, 2),
-            "roofline": dict(bound="mfma", achieved=round(tflops, 2),
-                             peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                             frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                             traffic=None if args.contiguous_pages else
-                             pmc_traffic("prefill_qwen3_prefill", PMC_PARTS["prefill"][1]),
-                             kernel="prefill attention",
-                             algorithmic_flops_per_call=fl, us_per_call=round(ms_pa * 1e3, 3)),
-            "prologue_bytes_per_call": pw.prologue_bytes(),
-        }
-        del gp_step, gp_attn
+        result["prefill"] = prefill_record(args)
 
     if not args.no_cpu_baseline:
-        log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s each)")
-        result["cpu_baseline"] = cpu_decode_baseline(args.cpu_seconds)
+        procs = args.cpu_processes or min(len(os.sched_getaffinity(0)), 16)
+        log(f"CPU oracle baselines (~{args.cpu_seconds:.0f} s each; all-cores leg: "
+            f"{procs} processes)")
+        result["cpu_baseline"] = cpu_decode_baseline(args.workload, args.cpu_seconds)
+        result["cpu_baseline_all_cores"] = cpu_decode_baseline(args.workload, args.cpu_seconds,
+                                                               procs)
         if "prefill" in result:
             result["prefill"]["cpu_baseline"] = cpu_prefill_baseline(args.cpu_seconds)
+            result["prefill"]["cpu_baseline_all_cores"] = cpu_prefill_baseline(
+                args.cpu_seconds, procs)
     else:
         result["cpu_baseline"] = None
     result["host"] = dict(cpu_count=os.cpu_count(),

@@ -111,7 +111,11 @@ typedef struct {
   const float* rope_sin;  /* device fp32 [max_pos][head_dim/2]          */
   int32_t max_pos;
   const void* k_raw;      /* device bf16 [total_tokens][n_kv][head_dim] */
-  const void* v_raw;      /* device bf16 [total_tokens][n_kv][head_dim] */
+  const void* v_raw;      /* device bf16 [total_tokens][n_kv][head_dim].
+                             k_raw and v_raw both NULL: nothing is appended
+                             (the keys are already in the pages, e.g. from an
+                             earlier call) and only q is normalised and
+                             rotated; k_norm_w and v_norm are then unused */
   void* q_out;            /* device bf16 [total_tokens][n_q][head_dim] or NULL:
                              where given, the normalised and rotated q' is
                              also written there (rows of padding sequences and
@@ -164,14 +168,22 @@ pkv_status pkv_append(const void* k_new, const void* v_new, const int32_t* slot,
  *   window   : 0 = full causal, W > 0 = sliding window of W keys incl. self
  *   out      : device bf16 [B][n_q_heads][head_dim]
  *   lse      : device fp32 [B][n_q_heads] natural-log sum-exp, or NULL
- *   workspace: device scratch of >= pkv_decode_workspace_size(...) bytes
- *              (NULL allowed when that size is 0) for the split partials; its
- *              contents need no initialisation.
- * The splits of a (row, kv head) count themselves in on per-device counters
- * inside the library (the last one merges); decode calls on one device must
- * therefore not overlap in time, whatever their workspaces.
- * n_q_heads / n_kv_heads must be an integer G in [1, 16] with G * head_dim <= 2048,
- * and B * n_kv_heads <= 65536 (PKV_ERR_UNSUPPORTED otherwise).  B == 0 is a no-op.
+ *   workspace: device scratch of >= pkv_decode_workspace_size(...) bytes,
+ *              16-byte aligned (NULL allowed when that size is 0).  It holds
+ *              the split partials (from its start; no initialisation needed)
+ *              and one arrival counter per (row, kv head) in its last
+ *              4 * B * n_kv_heads bytes: the splits of a (row, kv head) count
+ *              themselves in there and the last one merges.  Zero the whole
+ *              workspace once when it is created (before its first call,
+ *              outside any graph capture); every call leaves its counters at
+ *              zero again.  The counters are addressed back from
+ *              workspace + workspace_bytes, so a workspace reused by calls of
+ *              different shapes must be passed with the same workspace_bytes
+ *              each time.  Calls that overlap in time (other streams, other
+ *              graphs) need separate workspaces; calls with separate
+ *              workspaces share nothing.
+ * n_q_heads / n_kv_heads must be an integer G in [1, 16] with G * head_dim <= 2048
+ * (PKV_ERR_UNSUPPORTED otherwise).  B == 0 is a no-op.
  */
 pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slots,
                            const int32_t* seq_lens, int32_t B, int32_t max_seq_len_hint,
@@ -180,7 +192,8 @@ pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slot
                            int32_t window, void* out, float* lse, void* workspace,
                            size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace pkv_attn_decode needs for these sizes (0 = none). */
+/* Bytes of workspace pkv_attn_decode needs for these sizes (0 = none): the
+ * split partials plus 4 * B * n_kv_heads bytes of arrival counters. */
 size_t pkv_decode_workspace_size(int32_t B, int32_t n_q_heads, int32_t n_kv_heads,
                                  int32_t head_dim, int32_t max_seq_len_hint,
                                  int32_t window);

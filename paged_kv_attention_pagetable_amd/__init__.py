@@ -154,8 +154,11 @@ def attn_decode(q, slots, seq_lens, table, k_pool, v_pool, scale=None, window=0,
 
 
 def new_decode_workspace(nbytes, device="cuda"):
-    """A decode workspace of ``nbytes`` (contents need no initialisation)."""
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    """A zero-filled decode workspace of ``nbytes``, rounded up to 16 (its last
+    bytes hold the split arrival counters, which must start at zero; every
+    call leaves them at zero).  Pass the whole tensor to every call that uses
+    it."""
+    return torch.zeros(max((int(nbytes) + 15) // 16 * 16, 16), dtype=torch.uint8, device=device)
 
 
 def rope_table(max_pos, head_dim, theta, device="cuda", stream=None, rotary_fraction=1.0):
@@ -179,7 +182,9 @@ def attn_prefill(q, cu_seqlens, slots, table, k_pool, v_pool, scale=None, window
     without a gain; for K=V layers pass the raw k as ``v``): k (normalised and
     rotated) and v are appended before the attention, and q is normalised and rotated inside the
     attention kernel (``q`` itself is not modified; the normalised q' is also
-    written to ``q_out`` when given).
+    written to ``q_out`` when given).  With ``k`` and ``v`` None (or absent)
+    nothing is appended: the keys are already in the pages and only q is
+    normalised and rotated.
     """
     cd, pt = _cache(k_pool, v_pool, table)
     _bits16(q, "q")
@@ -200,9 +205,14 @@ def attn_prefill(q, cu_seqlens, slots, table, k_pool, v_pool, scale=None, window
     pro = None
     if prologue is not None:
         p = prologue
-        for name in ("k", "v", "q_norm_w", "k_norm_w"):
-            _bits16(p[name], name)
-        if tuple(p["k"].shape) != (T, cd.n_kv_heads, D) or p["v"].shape != p["k"].shape:
+        kr, vr = p.get("k"), p.get("v")
+        if (kr is None) != (vr is None):
+            raise ValueError("prologue: give both k and v, or neither")
+        kw = p.get("k_norm_w")
+        for name, t in (("k", kr), ("v", vr), ("q_norm_w", p["q_norm_w"]), ("k_norm_w", kw)):
+            if t is not None:
+                _bits16(t, name)
+        if kr is not None and (tuple(kr.shape) != (T, cd.n_kv_heads, D) or vr.shape != kr.shape):
             raise ValueError("prologue k / v must be [T, n_kv, head_dim]")
         cos, sin = p["cos"], p["sin"]
         if cos.dtype != torch.float32 or tuple(cos.shape[1:]) != (D // 2,) or \
@@ -213,9 +223,11 @@ def attn_prefill(q, cu_seqlens, slots, table, k_pool, v_pool, scale=None, window
             _bits16(q_out, "q_out")
             if tuple(q_out.shape) != (T, n_q, D):
                 raise ValueError("prologue q_out must be [T, n_q, head_dim]")
-        pro = Prologue(p["q_norm_w"].data_ptr(), p["k_norm_w"].data_ptr(), float(p["eps"]),
-                       cos.data_ptr(), sin.data_ptr(), cos.shape[0], p["k"].data_ptr(),
-                       p["v"].data_ptr(), q_out.data_ptr() if q_out is not None else None,
+        pro = Prologue(p["q_norm_w"].data_ptr(), kw.data_ptr() if kw is not None else None,
+                       float(p["eps"]), cos.data_ptr(), sin.data_ptr(), cos.shape[0],
+                       kr.data_ptr() if kr is not None else None,
+                       vr.data_ptr() if vr is not None else None,
+                       q_out.data_ptr() if q_out is not None else None,
                        1 if p.get("v_norm") else 0)
     check(lib().pkv_attn_prefill(_ptr(q), n_q, _ptr(cu_seqlens), _ptr(slots), _ptr(start_pos),
                                  n_seqs, T, int(max_seqlen_q_hint), pt, ctypes.byref(cd),

@@ -255,9 +255,6 @@ pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slot
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "%s: scale must be finite", fn);
   if (max_seq_len_hint < 1)
     return fail(PKV_ERR_INVALID_ARG, "%s: max_seq_len_hint must be >= 1", fn);
-  if ((long)B * g.n_kv > pkv::kDecodeMaxPairs)
-    return fail(PKV_ERR_UNSUPPORTED, "%s: B * n_kv_heads must be <= %d (got %ld)", fn,
-                pkv::kDecodeMaxPairs, (long)B * g.n_kv);
   if (B == 0) return PKV_OK;
   if (!q || !slots || !seq_lens || !k_pool || !v_pool || !out)
     return fail(PKV_ERR_INVALID_ARG, "%s: NULL tensor pointer", fn);
@@ -270,6 +267,9 @@ pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slot
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
     return fail(PKV_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", fn,
                 plan.ws_bytes, workspace ? workspace_bytes : (size_t)0);
+  // the merge moves partials with 8- and 16-byte device-scope accesses
+  if (plan.ws_bytes > 0 && misaligned16({workspace}))
+    return fail(PKV_ERR_INVALID_ARG, "%s: the workspace must be 16-byte aligned", fn);
   pkv::DecodeArgs a;
   a.q = static_cast<const pkv::bf16_t*>(q);
   a.n_q = n_q_heads;
@@ -292,6 +292,12 @@ pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slot
   a.waves = plan.waves;
   a.part_o = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
   a.part_ml = plan.ws_bytes ? a.part_o + plan.part_o_floats : nullptr;
+  // the counters sit at the end of the workspace as given, so every call that
+  // passes the same (workspace, workspace_bytes) finds them at the same place
+  a.arrivals_end =
+      plan.ws_bytes ? reinterpret_cast<uint32_t*>(
+                          (reinterpret_cast<uintptr_t>(workspace) + workspace_bytes) & ~(uintptr_t)3)
+                    : nullptr;
   a.out = static_cast<pkv::bf16_t*>(out);
   a.lse = lse;
   if (validation_on()) {
@@ -344,35 +350,40 @@ pkv_status pkv_attn_prefill(const void* q, int32_t n_q_heads, const int32_t* cu_
     st = launched(pkv::launch_validate_rows(tr, g, slots, nullptr, cu_seqlens, start_pos, n_seqs, s), fn);
     if (st != PKV_OK) return st;
   }
+  // k_raw == v_raw == NULL: the keys are already in the pages; only q gets
+  // its norm and rotation (inside the attention kernel)
+  const bool append_kv = pro && (pro->k_raw || pro->v_raw);
   if (pro) {
-    if (!pro->q_norm_w || !pro->k_norm_w || !pro->rope_cos || !pro->rope_sin || !pro->k_raw ||
-        !pro->v_raw)
+    if (!pro->q_norm_w || !pro->rope_cos || !pro->rope_sin ||
+        (append_kv && (!pro->k_norm_w || !pro->k_raw || !pro->v_raw)))
       return fail(PKV_ERR_INVALID_ARG, "%s: NULL pointer in the prologue", fn);
     if (pro->max_pos < 1) return fail(PKV_ERR_INVALID_ARG, "%s: prologue max_pos must be >= 1", fn);
     if ((total_tokens + 31) / 32 > 65535)
       return fail(PKV_ERR_UNSUPPORTED, "%s: with the prologue, total_tokens must be <= 2097120", fn);
     if (!(pro->eps >= 0.f) || !std::isfinite(pro->eps))
       return fail(PKV_ERR_INVALID_ARG, "%s: prologue eps must be finite and >= 0", fn);
-    pkv::PrologueArgs p;
-    p.k_raw = static_cast<const pkv::bf16_t*>(pro->k_raw);
-    p.v_raw = static_cast<const pkv::bf16_t*>(pro->v_raw);
-    p.k_w = static_cast<const pkv::bf16_t*>(pro->k_norm_w);
-    p.v_norm = pro->v_norm ? 1 : 0;
-    p.eps = pro->eps;
-    p.cos_t = pro->rope_cos;
-    p.sin_t = pro->rope_sin;
-    p.max_pos = pro->max_pos;
-    p.T = total_tokens;
-    p.cu_seqlens = cu_seqlens;
-    p.slots = slots;
-    p.start_pos = start_pos;
-    p.n_seqs = n_seqs;
-    p.pt = tr;
-    p.g = g;
-    p.kpool = static_cast<pkv::bf16_t*>(k_pool);
-    p.vpool = static_cast<pkv::bf16_t*>(v_pool);
-    st = launched(pkv::launch_prologue(p, s), fn);
-    if (st != PKV_OK) return st;
+    if (append_kv) {
+      pkv::PrologueArgs p;
+      p.k_raw = static_cast<const pkv::bf16_t*>(pro->k_raw);
+      p.v_raw = static_cast<const pkv::bf16_t*>(pro->v_raw);
+      p.k_w = static_cast<const pkv::bf16_t*>(pro->k_norm_w);
+      p.v_norm = pro->v_norm ? 1 : 0;
+      p.eps = pro->eps;
+      p.cos_t = pro->rope_cos;
+      p.sin_t = pro->rope_sin;
+      p.max_pos = pro->max_pos;
+      p.T = total_tokens;
+      p.cu_seqlens = cu_seqlens;
+      p.slots = slots;
+      p.start_pos = start_pos;
+      p.n_seqs = n_seqs;
+      p.pt = tr;
+      p.g = g;
+      p.kpool = static_cast<pkv::bf16_t*>(k_pool);
+      p.vpool = static_cast<pkv::bf16_t*>(v_pool);
+      st = launched(pkv::launch_prologue(p, s), fn);
+      if (st != PKV_OK) return st;
+    }
   }
   pkv::PrefillArgs a;
   a.q = static_cast<const pkv::bf16_t*>(q);

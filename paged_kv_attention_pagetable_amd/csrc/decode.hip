@@ -31,12 +31,14 @@
 // With several splits per row the partial (o, max, sum) of each workgroup
 // goes to the workspace and the last workgroup of the (row, kv head) to
 // arrive merges them, in fixed split order (bitwise deterministic whichever
-// workgroup merges).  The partials are written and read with device-scope
-// relaxed atomic accesses (sc1: coherent across the XCDs' L2s), each writer
-// waits for its stores to complete before it counts itself in, and the
-// counter wraps to zero on the last arrival -- no release fence, which on
-// gfx950 would write back the whole L2 per workgroup.  Optionally the new
-// token's K/V is appended first by the workgroup that owns the last key.
+// workgroup merges).  The arrival counters live in the caller's workspace
+// too (its last bytes), so calls with separate workspaces never share
+// state.  The partials are written and read with device-scope relaxed atomic
+// accesses (sc1: coherent across the XCDs' L2s), each writer waits for its
+// stores to complete before it counts itself in, and the counter wraps to
+// zero on the last arrival -- no release fence, which on gfx950 would write
+// back the whole L2 per workgroup (see finish).  Optionally the new token's
+// K/V is appended first by the workgroup that owns the last key.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -49,13 +51,6 @@ constexpr int kThreads = kDecodeWaves * 64;
 constexpr int kSegPages = 64;  // page ids staged in LDS per range segment
 constexpr int kMaxGD = 2048;   // (query heads per kv head) * head_dim, checked on the host
 constexpr int kMaxMergeUnits = 1024;  // cap on splits * G of one (row, kv head): bounds one merge
-
-// Split arrival counters, one per (row, kv head) of a call (index
-// b * n_kv + hk < kDecodeMaxPairs, host-checked).  Zero at load; every call
-// leaves them zero again (the increment wraps on the last arrival), so they
-// need no clearing.  Each GPU has its own copy; decode calls on one GPU must
-// not overlap in time.
-__device__ uint32_t g_split_arrivals[kDecodeMaxPairs];
 
 // Masks the bf16 elements e >= nvalid (0..8) of an 8-element operand.
 __device__ __forceinline__ u32x4 keep_first(u32x4 v, int nvalid) {
@@ -84,6 +79,7 @@ __device__ __forceinline__ int kst_swz(int r) {
 
 struct RowRange {
   int slot, L, lo, start, end, n_valid;
+  int L_in;  // seq_lens[b] as given (L is clamped to the slot's table capacity)
   bool idle;
 };
 
@@ -92,6 +88,7 @@ __device__ __forceinline__ RowRange row_range(const DecodeArgs& a, int b, int s,
   RowRange r;
   r.slot = slots[b];
   r.L = seq_lens[b];
+  r.L_in = r.L;
   r.idle = r.slot <= 0 || r.slot >= a.pt.max_slots || r.L <= 0;
   r.lo = r.start = r.end = r.n_valid = 0;
   if (r.idle) return r;
@@ -104,11 +101,15 @@ __device__ __forceinline__ RowRange row_range(const DecodeArgs& a, int b, int s,
   return r;
 }
 
-// Fused append: the workgroup owning key L-1 writes the new token of (b, hk).
+// Fused append: the workgroup owning the row's last key writes the new token
+// of (b, hk) at position seq_lens[b] - 1, as pkv_append would: a position
+// past the slot's table (a length beyond its capacity, a caller error) is
+// skipped, never folded onto the last row of the table.
 __device__ __forceinline__ void append_new_token(const DecodeArgs& a, const RowRange& r, int b,
                                                  int hk, int D) {
-  const int p = r.L - 1;
+  const int p = r.L_in - 1;
   const int lp = p >> a.g.log2ps;
+  if (lp >= a.pt.pps) return;
   const int page = a.pt.table[(size_t)r.slot * a.pt.pps + lp];
   if (page < 1 || page >= a.g.n_pages) return;
   const int ps = a.g.page_size;
@@ -232,15 +233,26 @@ __device__ void finish(const DecodeArgs& a, const RowRange& r, int b, int hk, in
     store_dev(a.part_ml + (pbase * G + g) * 2, Mof(g));
     store_dev(a.part_ml + (pbase * G + g) * 2 + 1, Lof(g));
   }
+  // Ordering of the partials before the arrival, as the gfx950 ISA gives it
+  // (not the HIP memory model's release/acquire): the partial stores above
+  // are device-scope (sc1) stores, which write through to the memory side
+  // that is coherent across all XCDs; s_waitcnt vmcnt(0) returns only once
+  // each has been acknowledged there, and the barrier extends that to the
+  // whole workgroup before thread 0's atomic increment is issued.  The merging
+  // workgroup reads every partial with device-scope (sc1) atomic loads, which
+  // are served from that same coherent level and never from a stale L1 / L2
+  // line, so no cache invalidation is needed either.  (A release fence instead
+  // writes back the XCD's whole L2 per workgroup: measured 3x slower.)
   __builtin_amdgcn_s_waitcnt(0);          // this thread's partial stores are complete
   __atomic_signal_fence(__ATOMIC_SEQ_CST);  // (and stay before the arrival below)
   __shared__ int s_last;
   __syncthreads();                        // ... and so are the whole workgroup's
   if (tid == 0) {
-    // wraps to 0 on the n_valid-th arrival, ready for the next call
-    const uint32_t old = __builtin_amdgcn_atomic_inc32(g_split_arrivals + (size_t)b * a.g.n_kv + hk,
-                                                       (uint32_t)(r.n_valid - 1), __ATOMIC_RELAXED,
-                                                       "agent");
+    // wraps to 0 on the n_valid-th arrival, ready for the next call that
+    // uses this workspace
+    uint32_t* ctr = a.arrivals_end - 1 - ((size_t)b * a.g.n_kv + hk);
+    const uint32_t old =
+        __builtin_amdgcn_atomic_inc32(ctr, (uint32_t)(r.n_valid - 1), __ATOMIC_RELAXED, "agent");
     s_last = old == (uint32_t)(r.n_valid - 1);
   }
   __syncthreads();
@@ -701,7 +713,10 @@ DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_h
   }
   const size_t units = (size_t)B * n_kv * p.max_splits * G;
   p.part_o_floats = (units * head_dim + 63) & ~(size_t)63;
-  p.ws_bytes = (p.part_o_floats + units * 2) * sizeof(float);
+  // partials from the start, then the (row, kv head) arrival counters, which
+  // the kernel addresses back from the workspace's end
+  p.ws_bytes = ((p.part_o_floats + units * 2) * sizeof(float) + (size_t)B * n_kv * 4 + 15) &
+               ~(size_t)15;
   return p;
 }
 

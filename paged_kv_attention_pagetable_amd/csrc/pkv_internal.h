@@ -74,6 +74,8 @@ struct DecodeArgs {
   int waves;             // wave64s per workgroup of the split kernel (4 or 8)
   float* part_o;         // [B][n_kv][max_splits][G][D]
   float* part_ml;        // [B][n_kv][max_splits][G][2]  (running max in log2 units, sum)
+  uint32_t* arrivals_end;  // one past the split arrival counters: pair b*n_kv+hk at
+                           // arrivals_end[-1 - (b*n_kv+hk)] (the workspace's last bytes)
   bf16_t* out;           // [B][n_q][D]
   float* lse;            // [B][n_q] or null
 };
@@ -173,8 +175,6 @@ struct DecodePlan {
   size_t ws_bytes;
   size_t part_o_floats;  // partial outputs first, then the (max, sum) pairs
 };
-// Largest B * n_kv of a decode call (split arrival counters on the device).
-constexpr int kDecodeMaxPairs = 1 << 16;
 DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_hint,
                        int window);
 

@@ -76,6 +76,10 @@ def test_decode_argument_checks_return_before_launch():
     assert _decode(B=64, n_q=32, cd=_desc(n_pages=100, ps=128, n_kv=8, D=128),
                    pt=_pt(max_slots=65, pps=32), hint=4096) == 4
     assert b"workspace" in pkv.lib().pkv_last_error()
+    # ... 16-byte aligned (the merge moves partials with 8- and 16-byte accesses)
+    assert _decode(B=64, n_q=32, cd=_desc(n_pages=100, ps=128, n_kv=8, D=128),
+                   pt=_pt(max_slots=65, pps=32), hint=4096, ws=P + 8, ws_bytes=need) == 1
+    assert b"workspace must be 16-byte aligned" in pkv.lib().pkv_last_error()
     # B == 0 is a valid no-op (nothing launched)
     assert _decode(B=0) == 0
 
@@ -85,6 +89,9 @@ def test_workspace_size_plan_is_monotone_and_zero_when_unsplit():
     a = pkv.decode_workspace_size(64, 24, 8, 128, 4096, 0)
     b = pkv.decode_workspace_size(64, 24, 8, 128, 4096, 512)   # window bounds the range
     assert a > 0 and b <= a
+    # the size covers the arrival counters (4 bytes per row and kv head) and
+    # is a multiple of 16
+    assert a % 16 == 0 and a >= 4 * 64 * 8
 
 
 def test_append_and_prefill_argument_checks():
@@ -102,6 +109,14 @@ def test_append_and_prefill_argument_checks():
     bad = _lib.Prologue(None, P, 1e-6, P, P, 16, P, P)
     assert L.pkv_attn_prefill(P, 4, P, P, None, 1, 8, 8, _pt(), ctypes.byref(cd), P, P, 0.1, 0,
                               ctypes.byref(bad), P, None, None, 0, None) == 1
+    # k without v (or v without k) is an error; both NULL = q-only prologue,
+    # which still needs q's norm weights and the rotary tables
+    half = _lib.Prologue(P, P, 1e-6, P, P, 16, P, None)
+    assert L.pkv_attn_prefill(P, 4, P, P, None, 1, 8, 8, _pt(), ctypes.byref(cd), P, P, 0.1, 0,
+                              ctypes.byref(half), P, None, None, 0, None) == 1
+    q_only_no_table = _lib.Prologue(P, None, 1e-6, None, P, 16, None, None)
+    assert L.pkv_attn_prefill(P, 4, P, P, None, 1, 8, 8, _pt(), ctypes.byref(cd), P, P, 0.1, 0,
+                              ctypes.byref(q_only_no_table), P, None, None, 0, None) == 1
     # the prologue's grid covers at most 65535 blocks of 32 tokens
     good = _lib.Prologue(P, P, 1e-6, P, P, 16, P, P)
     skew = _lib.Prologue(P, P, 1e-6, P + 4, P, 16, P, P)   # misaligned cos table
