@@ -192,6 +192,35 @@ pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slot
                            int32_t window, void* out, float* lse, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * pkv_attn_decode_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture with no allocator at hand, tight serving
+ * loops, harnesses that forbid hipMalloc): pkv_attn_decode with the split
+ * partials and arrival counters in a static scratch buffer inside the
+ * library instead of a workspace argument.  Same arguments, semantics and
+ * kernels as pkv_attn_decode (its results are bitwise those of
+ * pkv_attn_decode for the same inputs); the caller still passes every input
+ * and output.  The call allocates nothing and calls no allocating routine.
+ * - The buffer is PKV_DECODE_SCRATCH_BYTES (32 MiB) per device, held by each
+ *   device the library runs on until the process ends.  A call whose split
+ *   plan needs more (pkv_decode_workspace_size(...) above the limit) returns
+ *   PKV_ERR_WORKSPACE and enqueues nothing.
+ * - Every call on a device shares that device's buffer and leaves its
+ *   arrival counters at zero (they are zero when the library is loaded);
+ *   calls that overlap in time on one device (other streams, graphs
+ *   replayed concurrently) race and give undefined results.  Use
+ *   pkv_attn_decode with separate workspaces for concurrent calls.
+ * - The first call on a device looks the buffer's address up
+ *   (hipGetSymbolAddress; PKV_ERR_LAUNCH if that fails).
+ */
+#define PKV_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+pkv_status pkv_attn_decode_noalloc(const void* q, int32_t n_q_heads, const int32_t* slots,
+                                   const int32_t* seq_lens, int32_t B,
+                                   int32_t max_seq_len_hint, pkv_page_table pt,
+                                   const pkv_cache_desc* cd, void* k_pool, void* v_pool,
+                                   const void* k_new, const void* v_new, float scale,
+                                   int32_t window, void* out, float* lse, void* stream);
+
 /* Bytes of workspace pkv_attn_decode needs for these sizes (0 = none): the
  * split partials plus 4 * B * n_kv_heads bytes of arrival counters. */
 size_t pkv_decode_workspace_size(int32_t B, int32_t n_q_heads, int32_t n_kv_heads,

@@ -25,7 +25,7 @@ import torch
 from . import _lib
 from ._lib import CacheDesc, PageTableRef, Prologue, PkvError, check, lib
 
-__all__ = ["append", "attn_decode", "attn_prefill", "decode_workspace_size", "rope_table",
+__all__ = ["append", "attn_decode", "attn_decode_noalloc", "attn_prefill", "decode_workspace_size", "rope_table",
            "set_validation", "validation_flags", "VALIDATE_SLOT", "VALIDATE_PAGE", "VALIDATE_POS",
            "new_pools", "v_pool_shape", "new_decode_workspace", "PageAllocator", "DevicePageState",
            "RESERVE_NO_PAGES", "RESERVE_TOO_LONG", "RESERVE_BAD_STATE", "PkvError", "lib"]
@@ -150,6 +150,42 @@ def attn_decode(q, slots, seq_lens, table, k_pool, v_pool, scale=None, window=0,
                                 _ptr(v_pool), _ptr(k_new), _ptr(v_new), float(scale),
                                 int(window), _ptr(out), _ptr(lse), _ptr(workspace), wsize,
                                 _stream(stream, q.device)))
+    return out
+
+
+DECODE_SCRATCH_BYTES = 32 << 20   # the library's static scratch per device
+
+
+def attn_decode_noalloc(q, slots, seq_lens, table, k_pool, v_pool, out, scale=None, window=0,
+                        max_seq_len_hint=None, lse=None, k_new=None, v_new=None, stream=None):
+    """``attn_decode`` through ``pkv_attn_decode_noalloc``: no workspace, the split
+    partials go to the library's static per-device scratch, and nothing is
+    allocated here either, so ``out [B, n_q, D]`` (bf16) must be given.  Calls
+    that overlap in time on one device race (they share the scratch)."""
+    cd, pt = _cache(k_pool, v_pool, table)
+    _bits16(q, "q")
+    _bits16(out, "out")
+    _i32(slots, "slots")
+    _i32(seq_lens, "seq_lens")
+    B, n_q, D = q.shape
+    if D != cd.head_dim or tuple(out.shape) != (B, n_q, D):
+        raise ValueError("q / out shapes do not match the pools")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        _bits16(k_new, "k_new")
+        _bits16(v_new, "v_new")
+        if tuple(k_new.shape) != (B, cd.n_kv_heads, D) or v_new.shape != k_new.shape:
+            raise ValueError("k_new / v_new must be [B, n_kv, head_dim]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_seq_len_hint is None:
+        max_seq_len_hint = pt.pages_per_slot * cd.page_size
+    check(lib().pkv_attn_decode_noalloc(_ptr(q), n_q, _ptr(slots), _ptr(seq_lens), B,
+                                        int(max_seq_len_hint), pt, ctypes.byref(cd),
+                                        _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
+                                        float(scale), int(window), _ptr(out), _ptr(lse),
+                                        _stream(stream, q.device)))
     return out
 
 

@@ -63,6 +63,10 @@ _SIGS = {
                                   PageTableRef, ctypes.POINTER(CacheDesc), c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_float, c_int32, c_void_p, c_void_p,
                                   c_void_p, c_size_t, c_void_p]),
+    "pkv_attn_decode_noalloc": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32,
+                                          c_int32, PageTableRef, ctypes.POINTER(CacheDesc),
+                                          c_void_p, c_void_p, c_void_p, c_void_p, c_float,
+                                          c_int32, c_void_p, c_void_p, c_void_p]),
     "pkv_decode_workspace_size": (c_size_t, [c_int32] * 6),
     "pkv_attn_prefill": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int32,
                                    c_int32, c_int32, PageTableRef, ctypes.POINTER(CacheDesc),

@@ -231,13 +231,20 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t n_q_heads, int32_t n_kv_head
       .ws_bytes;
 }
 
-pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slots,
-                           const int32_t* seq_lens, int32_t B, int32_t max_seq_len_hint,
-                           pkv_page_table pt, const pkv_cache_desc* cd, void* k_pool,
-                           void* v_pool, const void* k_new, const void* v_new, float scale,
-                           int32_t window, void* out, float* lse, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-  const char* fn = "pkv_attn_decode";
+}  // extern "C"
+
+namespace {
+
+// Shared body of pkv_attn_decode and pkv_attn_decode_noalloc.  no_alloc: the
+// split partials and arrival counters go to the library's static scratch
+// buffer of this device instead of `workspace`.
+pkv_status attn_decode_impl(const char* fn, const void* q, int32_t n_q_heads,
+                            const int32_t* slots, const int32_t* seq_lens, int32_t B,
+                            int32_t max_seq_len_hint, pkv_page_table pt,
+                            const pkv_cache_desc* cd, void* k_pool, void* v_pool,
+                            const void* k_new, const void* v_new, float scale, int32_t window,
+                            void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream, bool no_alloc) {
   if (B < 0) return fail(PKV_ERR_INVALID_ARG, "%s: B must be >= 0 (got %d)", fn, B);
   if (B > 65535) return fail(PKV_ERR_UNSUPPORTED, "%s: B must be <= 65535 (got %d)", fn, B);
   pkv::PoolGeom g;
@@ -264,6 +271,18 @@ pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slot
     return fail(PKV_ERR_INVALID_ARG, "%s: bf16 buffers must be 16-byte aligned", fn);
   const pkv::DecodePlan plan =
       pkv::plan_decode(B, n_q_heads, g.n_kv, g.head_dim, max_seq_len_hint, window);
+  if (no_alloc && plan.ws_bytes > 0) {
+    if (plan.ws_bytes > pkv::kDecodeScratchBytes)
+      return fail(PKV_ERR_WORKSPACE,
+                  "%s: this call's split partials need %zu bytes, more than the %zu-byte "
+                  "static scratch; use pkv_attn_decode with a workspace",
+                  fn, plan.ws_bytes, pkv::kDecodeScratchBytes);
+    const hipError_t e = pkv::decode_scratch(&workspace);
+    if (e != hipSuccess)
+      return fail(PKV_ERR_LAUNCH, "%s: no static scratch on this device: %s", fn,
+                  hipGetErrorString(e));
+    workspace_bytes = pkv::kDecodeScratchBytes;
+  }
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
     return fail(PKV_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", fn,
                 plan.ws_bytes, workspace ? workspace_bytes : (size_t)0);
@@ -307,6 +326,32 @@ pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slot
     if (st != PKV_OK) return st;
   }
   return launched(pkv::launch_decode(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slots,
+                           const int32_t* seq_lens, int32_t B, int32_t max_seq_len_hint,
+                           pkv_page_table pt, const pkv_cache_desc* cd, void* k_pool,
+                           void* v_pool, const void* k_new, const void* v_new, float scale,
+                           int32_t window, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return attn_decode_impl("pkv_attn_decode", q, n_q_heads, slots, seq_lens, B, max_seq_len_hint,
+                          pt, cd, k_pool, v_pool, k_new, v_new, scale, window, out, lse,
+                          workspace, workspace_bytes, stream, false);
+}
+
+pkv_status pkv_attn_decode_noalloc(const void* q, int32_t n_q_heads, const int32_t* slots,
+                                   const int32_t* seq_lens, int32_t B,
+                                   int32_t max_seq_len_hint, pkv_page_table pt,
+                                   const pkv_cache_desc* cd, void* k_pool, void* v_pool,
+                                   const void* k_new, const void* v_new, float scale,
+                                   int32_t window, void* out, float* lse, void* stream) {
+  return attn_decode_impl("pkv_attn_decode_noalloc", q, n_q_heads, slots, seq_lens, B,
+                          max_seq_len_hint, pt, cd, k_pool, v_pool, k_new, v_new, scale, window,
+                          out, lse, nullptr, 0, stream, true);
 }
 
 pkv_status pkv_attn_prefill(const void* q, int32_t n_q_heads, const int32_t* cu_seqlens,

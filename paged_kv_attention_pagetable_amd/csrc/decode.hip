@@ -39,6 +39,8 @@
 // zero on the last arrival -- no release fence, which on gfx950 would write
 // back the whole L2 per workgroup (see finish).  Optionally the new token's
 // K/V is appended first by the workgroup that owns the last key.
+#include <mutex>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -718,6 +720,37 @@ DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_h
   p.ws_bytes = ((p.part_o_floats + units * 2) * sizeof(float) + (size_t)B * n_kv * 4 + 15) &
                ~(size_t)15;
   return p;
+}
+
+// The static scratch of pkv_attn_decode_noalloc: split partials from the
+// start, arrival counters in its last bytes (zero when the code object is
+// loaded; every call leaves them at zero).  In host code `scratch` names a
+// host-side stand-in, never the device memory: its device address is taken
+// with hipGetSymbolAddress once per device, with that device current, and
+// only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {

@@ -178,6 +178,12 @@ struct DecodePlan {
 DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_hint,
                        int window);
 
+// Static split-K scratch of pkv_attn_decode_noalloc: one buffer of this many
+// bytes per device, inside the library's code object.  decode_scratch gives
+// the current device's copy (its address is looked up once per device).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t decode_scratch(void** ptr);
+
 // Query tokens per prefill workgroup for a GQA ratio.
 int prefill_q_tokens(int G, int head_dim);
 
