@@ -97,9 +97,23 @@ __device__ __forceinline__ RowRange row_range(const DecodeArgs& a, int b, int s,
   r.L = min(r.L, a.pt.pps * a.g.page_size);
   r.lo = a.window > 0 ? max(0, r.L - a.window) : 0;
   const int base = r.lo & ~31;
-  r.n_valid = min(a.max_splits, (r.L - base + a.split_tokens - 1) / a.split_tokens);
-  r.start = base + s * a.split_tokens;
-  r.end = (s == a.max_splits - 1) ? r.L : min(r.L, r.start + a.split_tokens);
+  const int span = r.L - base;
+  r.n_valid = min(a.max_splits, (span + a.split_tokens - 1) / a.split_tokens);
+  if (a.window > 0) {
+    // Sliding window: split 0 takes the range's remainder (span - (n_valid -
+    // 1) full splits, rounded up to whole 32-key chunks; beyond max_splits
+    // splits it absorbs the excess), splits 1 .. full split_tokens after it.
+    // A window range is about one window long, so the remainder is a sliver
+    // of keys; as split 0 it is the last workgroup of its row to start
+    // instead of the first (measured 7 % faster on the Gemma sliding layers;
+    // on full-causal rows the plain layout below measured 1-3 % faster).
+    const int first = (span - (r.n_valid - 1) * a.split_tokens + 31) & ~31;
+    r.start = s == 0 ? base : base + first + (s - 1) * a.split_tokens;
+    r.end = min(r.L, s == 0 ? base + first : r.start + a.split_tokens);
+  } else {
+    r.start = base + s * a.split_tokens;
+    r.end = (s == a.max_splits - 1) ? r.L : min(r.L, r.start + a.split_tokens);
+  }
   return r;
 }
 

@@ -419,6 +419,8 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const Item& it,
   if (ps >= kChunk) {
     // The chunk lies inside one page: one (scalar) page id and source base;
     // the lane offsets within the page are fixed.
+    int lane_o = lane;
+    if constexpr (D >= 256) asm volatile("" : "+v"(lane_o));
     const int page = __builtin_amdgcn_readfirstlane(max(s_pg[(j0 >> log2ps) - it.pg0], 0));
     const size_t base = (size_t)page * page_stride;
     const int in_pg = j0 & (ps - 1);
@@ -426,12 +428,12 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const Item& it,
     const uint8_t* vs = reinterpret_cast<const uint8_t*>(vbase + base + (size_t)in_pg * D);  // group in_pg/32
 #pragma unroll
     for (int k = 0; k < dma_per_wave<D>(); ++k)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const bf16_t*>(ks + dma_k_off<D>(k, lane, w)),
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const bf16_t*>(ks + dma_k_off<D>(k, lane_o, w)),
                                        (lds_void_ptr)(tK + (w * dma_per_wave<D>() + k) * 1024),
                                        16, 0, 0);
 #pragma unroll
     for (int k = 0; k < dma_per_wave<D>(); ++k)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const bf16_t*>(vs + dma_v_off<D>(k, lane, w)),
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const bf16_t*>(vs + dma_v_off<D>(k, lane_o, w)),
                                        (lds_void_ptr)(tV + (w * dma_per_wave<D>() + k) * 1024),
                                        16, 0, 0);
     return;

@@ -25,6 +25,8 @@ CASES = {
     "d512_prefix_w40_ps16": (16, 4, 512, 16, [50, 33], [20, 0], 40),
     "g1_ps16": (4, 4, 128, 16, [90, 31], None, 0),
     "g16": (16, 1, 64, 32, [40, 9], None, 0),
+    "kv16_g2": (32, 16, 64, 32, [40, 90, 7], None, 0),
+    "kv3_g4": (12, 3, 128, 64, [70, 130], [0, 9], 0),
     "slot0_pad": (8, 2, 64, 16, [20, 12, 30], None, 0),
     "ps256_prefix": (16, 4, 128, 256, [300, 520, 17], [0, 250, 0], 0),
     "d64_w100_prefix": (8, 2, 64, 64, [150, 64], [30, 0], 100),
