@@ -245,6 +245,18 @@ class PrefillWorkload:
         c = self.c
         return int((2 * 2 * c["head_dim"] * c["n_q"] * L * (L + 1) // 2).sum())
 
+    def attn_bytes(self):
+        """Compulsory HBM bytes of one attention call: q read and out written once
+        ([T][n_q][D] bf16 each), every sequence's K and V rows (its cached
+        prefix and its prompt) read once, and its page ids."""
+        c, case = self.c, self.case
+        L = np.diff(case.cu_seqlens).astype(np.int64)
+        keys = L + np.asarray(case.start_pos, dtype=np.int64)
+        qo = case.T * c["n_q"] * c["head_dim"] * 2 * 2
+        kv = int(keys.sum()) * c["n_kv"] * c["head_dim"] * 2 * 2
+        pages = int(np.ceil(keys / c["page_size"]).sum()) * 4
+        return qo + kv + pages
+
     def prologue_bytes(self):
         """Bytes of the prologue kernel: k and v rows read and written (q's norm
         and rotation run inside the attention kernel, which reads q anyway)."""
@@ -398,8 +410,7 @@ def source_sha(names):
     return h.hexdigest()[:16]
 
 
-def pmc_traffic(part):
-    """HBM bytes per call from a committed rocprofv3 PMC summary, if current."""
+def _pmc_record(part):
     path = os.path.join(PROFILES, f"{part}_pmc.json")
     if not os.path.exists(path):
         return None
@@ -407,7 +418,19 @@ def pmc_traffic(part):
         rec = json.load(f)
     if rec.get("source_sha") != source_sha(PMC_PARTS[part][1]):
         return None   # kernel changed since the counters were taken
-    return rec.get("hbm_bytes_per_call")
+    return rec
+
+
+def pmc_traffic(part, instance=None):
+    """HBM bytes per call from a committed rocprofv3 PMC summary, if current:
+    of the part's counted kernels, or of one kernel ``instance`` of it."""
+    rec = _pmc_record(part)
+    if rec is None:
+        return None
+    if instance is None:
+        return rec.get("hbm_bytes_per_call")
+    k = rec.get("kernels", {}).get(instance)
+    return None if k is None else k["fetch_bytes"] + k["write_bytes"]
 
 
 # ----------------------------------------------------------------------------
@@ -752,6 +775,8 @@ def decode_record(name, args, headline=False):
                 us_per_call=round(ms * 1e3, 3), algorithmic_bytes_per_call=int(b),
                 achieved=round(b / (ms * 1e-3) / 1e9, 1),
                 frac=round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                traffic=None if args.contiguous_pages else pmc_traffic(
+                    f"decode_{name}", f"decode_dimsplit_kernel<{D}>"),
                 window=max(ly["window"] for ly in lys))
             del g
     if args.attn_only:
@@ -782,6 +807,7 @@ def prefill_record(args):
     ms_pa = time_graph(gp_attn, args.kernel_reps, 2) / pw.n_calls
     ms_fq = time_graph(gp_fq, args.kernel_reps, 2) / pw.n_calls
     fl = pw.flops_per_call()
+    ab = pw.attn_bytes()
 
     def roof(ms, part, kernel):
         tf = fl / (ms * 1e-3) / 1e12
@@ -802,6 +828,16 @@ def prefill_record(args):
         "roofline_fused_q": roof(ms_fq, "prefill_fused_q_qwen3_prefill",
                                  "prefill attention with the fused q RMSNorm + RoPE (the "
                                  "instance a prefill layer with the prologue runs)"),
+        # The same kernel against the HBM roofline: its arithmetic intensity
+        # (FLOPs per compulsory byte: q and out once, each sequence's K/V once)
+        # lies below the bf16 ridge, so its bytes bound it before its FLOPs.
+        "roofline_hbm": dict(
+            bound="hbm", achieved=round(ab / (ms_pa * 1e-3) / 1e9, 1), peak=HBM_PEAK_GBS,
+            unit="GB/s", frac=round(ab / (ms_pa * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            traffic=None if args.contiguous_pages else pmc_traffic("prefill_qwen3_prefill"),
+            algorithmic_bytes_per_call=ab, us_per_call=round(ms_pa * 1e3, 3),
+            arithmetic_intensity=round(fl / ab, 1),
+            ridge=round(MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9), 1)),
         "prologue_us_per_call": round((ms_p / pw.n_calls - ms_fq) * 1e3, 3),
         "prologue_bytes_per_call": pw.prologue_bytes(),
     }
