@@ -117,27 +117,138 @@ __device__ __forceinline__ RowRange row_range(const DecodeArgs& a, int b, int s,
   return r;
 }
 
-// Fused append: the workgroup owning the row's last key writes the new token
-// of (b, hk) at position seq_lens[b] - 1, as pkv_append would: a position
-// past the slot's table (a length beyond its capacity, a caller error) is
-// skipped, never folded onto the last row of the table.
-__device__ __forceinline__ void append_new_token(const DecodeArgs& a, const RowRange& r, int b,
-                                                 int hk, int D) {
-  const int p = r.L_in - 1;
-  const int lp = p >> a.g.log2ps;
-  if (lp >= a.pt.pps) return;
-  const int page = a.pt.table[(size_t)r.slot * a.pt.pps + lp];
-  if (page < 1 || page >= a.g.n_pages) return;
-  const int ps = a.g.page_size;
-  const size_t blk = (size_t)ps * D;
-  const size_t dst = (size_t)page * a.g.n_kv * blk + hk * blk;
-  const int row = p & (ps - 1);
-  const size_t src = ((size_t)b * a.g.n_kv + hk) * D;
-  for (int i = threadIdx.x; i < D / 8; i += blockDim.x)
-    store16(a.kpool_w + dst + (size_t)row * D + 8 * i, load16(a.k_new + src + 8 * i));
-  for (int d = threadIdx.x; d < D; d += blockDim.x)
-    a.vpool_w[dst + v_elem_offset(d, row, D, a.g.log2ps)] = a.v_new[src + d];
+// Fused append (k_new / v_new given).  The workgroup whose key range ends at
+// the row's last key L-1 owns the new token of (b, hk), at position
+// seq_lens[b] - 1 as pkv_append would place it; a position past the slot's
+// table (a length beyond its capacity, a caller error) is skipped, never
+// folded onto the last row of the table.  The token never makes a round trip
+// through the pool inside the call:
+//   - its K and V rows are loaded into registers when the workgroup starts
+//     (NewTok::load), overlapping the row's slot and length loads, and moved
+//     to LDS with the first page staging (NewTok::stage);
+//   - the chunk holding key L-1 takes them from there: the K row into the
+//     wave's stage once its copies have landed, the V values into the MFMA
+//     operand registers (NewTok::patch), so the operands are bit for bit what
+//     a read of the appended pool would give;
+//   - V (page size >= 32): that chunk loads its whole 32-key group of V
+//     unmasked (the lanes past the last key address the same page), takes
+//     the new key in, and writes the group's 64-byte rows back whole
+//     (NewTok::store_v_rows) before masking the operands.  One 2-byte store
+//     per dim, as a plain append does, is a partial write that the memory
+//     must read, merge and write back: measured 5 us of the Llama call.
+//   - K (and V for smaller pages): written after the split's result
+//     (NewTok::store), where no later wait of the workgroup depends on them.
+//     (Written first, the stores sat in front of every chunk load in the
+//     in-order memory counter; written last with their own loads, the
+//     dependent round trips lengthened the appending workgroups instead.)
+// v is kept per wave slice of DW dims as [lane % 16][dt]: the eight V values
+// a patching lane needs (dims d0 + 16*dt + lane%16) are one 16-byte read.
+template <int D>
+struct NewTokLds {
+  bf16_t k[D];
+  bf16_t v[D];
+};
+template <int DW>
+__device__ __forceinline__ int newtok_v_index(int d) {
+  const int rem = d % DW;
+  return d - rem + (rem % 16) * (DW / 16) + rem / 16;
 }
+
+template <int D>
+struct NewTok {
+  static constexpr int kNV = (D + 255) / 256;  // v values per thread (>= 256 threads)
+  bool on = false;  // this workgroup appends (uniform)
+  int page = -1;    // physical page of key L-1, -1 if unmapped (then nothing is written)
+  u32x4 k{0, 0, 0, 0};
+  bf16_t v[kNV] = {};
+
+  __device__ __forceinline__ void load(const DecodeArgs& a, const RowRange& r, int b, int hk) {
+    on = a.k_new && r.end == r.L && ((r.L_in - 1) >> a.g.log2ps) < a.pt.pps;
+    if (!on) return;
+    const size_t src = ((size_t)b * a.g.n_kv + hk) * D;
+    if ((int)threadIdx.x < D / 8) k = load16(a.k_new + src + 8 * threadIdx.x);
+#pragma unroll
+    for (int i = 0; i < kNV; ++i) {
+      const int d = threadIdx.x + 256 * i;
+      if (d < D) v[i] = a.v_new[src + d];
+    }
+  }
+  // During the first page staging (a barrier follows); DW = the dims of a
+  // wave's slice (D for the key-split kernel).
+  template <int DW>
+  __device__ __forceinline__ void stage(NewTokLds<D>& L) const {
+    if (!on) return;
+    if ((int)threadIdx.x < D / 8) store16(L.k + 8 * threadIdx.x, k);
+#pragma unroll
+    for (int i = 0; i < kNV; ++i) {
+      const int d = threadIdx.x + 256 * i;
+      if (d < D) L.v[newtok_v_index<DW>(d)] = v[i];
+    }
+  }
+  // After the staging of the segment that ends the range (s_pg of it).
+  __device__ __forceinline__ void find_page(const RowRange& r, int log2ps, int p0, const int* s_pg) {
+    if (on) page = __builtin_amdgcn_readfirstlane(s_pg[((r.L - 1) >> log2ps) - p0]);
+  }
+  // Whether the chunk at t0 holds the new key (and the key is on a page).
+  __device__ __forceinline__ bool in_chunk(const RowRange& r, int t0) const {
+    return on && page >= 0 && t0 == ((r.L - 1) & ~31);
+  }
+  // The wave's K stage row and V operands of the chunk at t0: dims [d0, d0 +
+  // DW) of the key, stage rows of 2*DW bytes swizzled by kst_swz<DW>, V^T rows
+  // d0 + 16*dt + (lane%16) holding keys t0 + 8*(lane/16) ...
+  template <int DW, class SWZ>
+  __device__ __forceinline__ void patch(const RowRange& r, int t0, int d0, uint8_t* kst, SWZ swz,
+                                        const NewTokLds<D>& L, u32x4 (&vop)[DW / 16]) const {
+    const int lane = threadIdx.x & 63, qc = lane & 15, quad = lane >> 4;
+    const int rr = r.L - 1 - t0;
+    for (int c = lane; c < DW / 8; c += 64)
+      store16(kst + rr * (2 * DW) + 16 * (c ^ swz(rr)), load16(L.k + d0 + 8 * c));
+    if (quad == (rr >> 3)) {
+      const int e = rr & 7;
+      bf16_t xs[DW / 16];
+      static_assert(DW / 16 == 8 || DW / 16 == 4, "one 16- or 8-byte read");
+      if constexpr (DW / 16 == 8)
+        *reinterpret_cast<u32x4*>(xs) = load16(L.v + d0 + qc * (DW / 16));
+      else
+        *reinterpret_cast<uint64_t*>(xs) = *reinterpret_cast<const uint64_t*>(L.v + d0 + qc * (DW / 16));
+#pragma unroll
+      for (int dt = 0; dt < DW / 16; ++dt) {
+        const uint32_t x = xs[dt];
+        u32x4 o = vop[dt];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          if (e == 2 * h) o[h] = (o[h] & 0xffff0000u) | x;
+          if (e == 2 * h + 1) o[h] = (o[h] & 0x0000ffffu) | (x << 16);
+        }
+        vop[dt] = o;
+      }
+    }
+  }
+  // After the split's result: the pool rows.
+  template <int DW>
+  __device__ __forceinline__ void store(const DecodeArgs& a, const RowRange& r, int hk,
+                                        const NewTokLds<D>& L) const {
+    if (!on || page < 0) return;
+    const int ps = a.g.page_size;
+    const size_t blk = (size_t)ps * D;
+    const size_t dst = (size_t)page * a.g.n_kv * blk + hk * blk;
+    const int row = (r.L - 1) & (ps - 1);
+    for (int i = threadIdx.x; i < D / 8; i += blockDim.x)
+      store16(a.kpool_w + dst + (size_t)row * D + 8 * i, load16(L.k + 8 * i));
+    if (ps >= 32) return;  // V went out whole with its chunk (store_v_rows)
+    for (int d = threadIdx.x; d < D; d += blockDim.x)
+      a.vpool_w[dst + v_elem_offset(d, row, D, a.g.log2ps)] = L.v[newtok_v_index<DW>(d)];
+  }
+  // Page size >= 32, in the chunk holding the new key, after patch(): each
+  // lane's 16 bytes of V (rows d0 + 16*dt + lane%16, the 8 keys of its
+  // quarter of the group) back to the address it loaded them from; the four
+  // quarters make each row's 64 bytes.
+  template <int DW>
+  __device__ __forceinline__ void store_v_rows(bf16_t* vrow0, int lgv, const u32x4 (&vop)[DW / 16]) const {
+#pragma unroll
+    for (int dt = 0; dt < DW / 16; ++dt) store16(vrow0 + ((size_t)16 * dt << lgv), vop[dt]);
+  }
+};
 
 // Stages the page ids of logical pages [p0, p0 + n) of the row into LDS.
 __device__ __forceinline__ void stage_pages(const DecodeArgs& a, const int32_t* trow, int p0, int n,
@@ -302,6 +413,7 @@ void decode_keysplit_kernel(const int32_t* slots, const int32_t* seq_lens, const
   __shared__ int s_pg[kSegPages];
   __shared__ float s_ml[2 * NW * 16];             // [wave][16] max, then sum
   __shared__ float s_red[NW * 16 + 32];
+  __shared__ __attribute__((aligned(16))) NewTokLds<D> s_new;
   constexpr int kStage = 32 * D * 2;              // bytes of a wave's K stage
   const int hk = blockIdx.x, b = blockIdx.y, s = max_splits - 1 - (int)blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -313,7 +425,8 @@ void decode_keysplit_kernel(const int32_t* slots, const int32_t* seq_lens, const
     return;
   }
   if (s >= r.n_valid) return;  // past the row's last key: not counted by the merge
-  if (a.k_new && r.end == r.L) append_new_token(a, r, b, hk, D);
+  NewTok<D> nt;
+  nt.load(a, r, b, hk);
 
   const int ps = a.g.page_size, log2ps = a.g.log2ps;
   const int32_t* trow = table + (size_t)r.slot * a.pt.pps;
@@ -336,9 +449,11 @@ void decode_keysplit_kernel(const int32_t* slots, const int32_t* seq_lens, const
   for (int seg0 = r.start; seg0 < r.end; seg0 += seg_tokens) {
     const int seg1 = min(r.end, seg0 + seg_tokens);
     const int p0 = seg0 >> log2ps;
-    __syncthreads();  // previous segment's page ids consumed; orders the fused append
+    __syncthreads();  // previous segment's page ids consumed
     stage_pages(a, trow, p0, ((seg1 - 1) >> log2ps) - p0 + 1, s_pg);
+    if (seg0 == r.start) nt.template stage<D>(s_new);
     __syncthreads();
+    if (seg1 == r.end) nt.find_page(r, log2ps, p0, s_pg);
     if (seg0 == r.start) {
       // Columns qc >= G repeat head G-1: MFMA columns never mix, and those
       // are never stored.  (Zeroing them here would wait for q before the
@@ -381,18 +496,23 @@ void decode_keysplit_kernel(const int32_t* slots, const int32_t* seq_lens, const
       const int tv = t0 + 8 * quad;
       const int vpage = tv < seg1 ? s_pg[(tv >> log2ps) - p0] : -1;
       const int nvalid = seg1 - tv;
+      const bool app = nt.in_chunk(r, t0), vrows = app && ps >= 32;
       u32x4 vop[D / 16];
-      {
-        // V^T row d = 16*dt + qc, keys tv .. tv+7 (inside one key group)
-        const bf16_t* vp = vbase + (size_t)max(vpage, 0) * page_stride + v_elem_offset(qc, tv & (ps - 1), D, log2ps);
+      // V^T row d = 16*dt + qc, keys tv .. tv+7 (inside one key group); the
+      // new key's chunk reads its whole group from the new key's page
+      const bf16_t* vp = vbase + (size_t)(vrows ? nt.page : max(vpage, 0)) * page_stride +
+                         v_elem_offset(qc, tv & (ps - 1), D, log2ps);
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const u32x4 v = load16_nt(vp + ((size_t)16 * dt << lgv));
-          vop[dt] = vpage >= 0 ? (nvalid < 8 ? keep_first(v, nvalid) : v) : u32x4{0, 0, 0, 0};
-        }
-      }
+      for (int dt = 0; dt < D / 16; ++dt) vop[dt] = load16_nt(vp + ((size_t)16 * dt << lgv));
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the K copies have landed in the stage
       __atomic_signal_fence(__ATOMIC_SEQ_CST);  // (and the stage reads stay after it)
+      if (app) {
+        nt.template patch<D>(r, t0, 0, kst, kst_swz<D>, s_new, vop);
+        if (vrows) nt.template store_v_rows<D>(a.vpool_w + (vp - a.vpool), lgv, vop);
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        vop[dt] = vpage >= 0 ? (nvalid < 8 ? keep_first(vop[dt], nvalid) : vop[dt]) : u32x4{0, 0, 0, 0};
       // ---- S^T = K Q^T; MFMA rg row m holds key 8*(m/4) + 4*rg + m%4
       f32x4 S[2];
 #pragma unroll
@@ -478,6 +598,7 @@ void decode_keysplit_kernel(const int32_t* slots, const int32_t* seq_lens, const
   auto Mof = [&](int g) { return s_red[NW * 16 + g]; };
   auto Lof = [&](int g) { return s_red[NW * 16 + 16 + g]; };
   finish<D>(a, r, b, hk, s, o_val, Mof, Lof);
+  nt.template store<D>(a, r, hk, s_new);
 }
 
 // ---------------------------------------------------------------------------
@@ -504,6 +625,7 @@ void decode_dimsplit_kernel(const int32_t* slots, const int32_t* seq_lens, const
   __shared__ __attribute__((aligned(16))) uint8_t s_stage[kDecodeWaves * kStage];
   float* const s_o = reinterpret_cast<float*>(s_stage);
   __shared__ float s_ml[32];
+  __shared__ __attribute__((aligned(16))) NewTokLds<D> s_new;
   const int hk = blockIdx.x, b = blockIdx.y, s = max_splits - 1 - (int)blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int qc = lane & 15, quad = lane >> 4;
@@ -514,7 +636,8 @@ void decode_dimsplit_kernel(const int32_t* slots, const int32_t* seq_lens, const
     return;
   }
   if (s >= r.n_valid) return;  // past the row's last key: not counted by the merge
-  if (a.k_new && r.end == r.L) append_new_token(a, r, b, hk, D);
+  NewTok<D> nt;
+  nt.load(a, r, b, hk);
 
   const int dw0 = w * DW;
   u32x4 qreg[DW / 32];  // loaded after the first page staging (see the key-split kernel)
@@ -539,7 +662,9 @@ void decode_dimsplit_kernel(const int32_t* slots, const int32_t* seq_lens, const
     const int p0 = seg0 >> log2ps;
     __syncthreads();
     stage_pages(a, trow, p0, ((seg1 - 1) >> log2ps) - p0 + 1, s_pg);
+    if (seg0 == r.start) nt.template stage<DW>(s_new);
     __syncthreads();
+    if (seg1 == r.end) nt.find_page(r, log2ps, p0, s_pg);
     if (seg0 == r.start) {
 #pragma unroll
       for (int c = 0; c < DW / 32; ++c) qreg[c] = load16(qrow + 32 * c);  // (qc >= G: head G-1, unused)
@@ -574,17 +699,23 @@ void decode_dimsplit_kernel(const int32_t* slots, const int32_t* seq_lens, const
       const int tv = t0 + 8 * quad;
       const int vpage = tv < seg1 ? s_pg[(tv >> log2ps) - p0] : -1;
       const int nvalid = seg1 - tv;
-      // V^T row d = dw0 + 16*dt + qc, keys tv .. tv+7 (inside one key group)
-      const bf16_t* vp =
-          vbase + (size_t)max(vpage, 0) * page_stride + v_elem_offset(dw0 + qc, tv & (ps - 1), D, log2ps);
+      const bool app = nt.in_chunk(r, t0), vrows = app && ps >= 32;
+      // V^T row d = dw0 + 16*dt + qc, keys tv .. tv+7 (inside one key group);
+      // the new key's chunk reads its whole group from the new key's page
+      const bf16_t* vp = vbase + (size_t)(vrows ? nt.page : max(vpage, 0)) * page_stride +
+                         v_elem_offset(dw0 + qc, tv & (ps - 1), D, log2ps);
       u32x4 vop[DW / 16];
 #pragma unroll
-      for (int dt = 0; dt < DW / 16; ++dt) {
-        const u32x4 v = load16_nt(vp + ((size_t)16 * dt << lgv));
-        vop[dt] = vpage >= 0 ? (nvalid < 8 ? keep_first(v, nvalid) : v) : u32x4{0, 0, 0, 0};
-      }
+      for (int dt = 0; dt < DW / 16; ++dt) vop[dt] = load16_nt(vp + ((size_t)16 * dt << lgv));
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the K copies have landed in the stage
       __atomic_signal_fence(__ATOMIC_SEQ_CST);  // (and the stage reads stay after it)
+      if (app) {
+        nt.template patch<DW>(r, t0, dw0, kst, kst_swz<DW>, s_new, vop);
+        if (vrows) nt.template store_v_rows<DW>(a.vpool_w + (vp - a.vpool), lgv, vop);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DW / 16; ++dt)
+        vop[dt] = vpage >= 0 ? (nvalid < 8 ? keep_first(vop[dt], nvalid) : vop[dt]) : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int rg = 0; rg < 2; ++rg) {
         const int rr = 8 * (qc >> 2) + 4 * rg + (qc & 3);
@@ -652,6 +783,7 @@ void decode_dimsplit_kernel(const int32_t* slots, const int32_t* seq_lens, const
   auto Mof = [&](int g) { return s_ml[g]; };
   auto Lof = [&](int g) { return s_ml[16 + g]; };
   finish<D>(a, r, b, hk, s, o_val, Mof, Lof);
+  nt.template store<DW>(a, r, hk, s_new);
 }
 
 // Dynamic LDS of the key-split kernel: the larger of the waves' K stages and
