@@ -626,7 +626,12 @@ __device__ __forceinline__ void chunk_math(const PrefillArgs& a, const uint8_t* 
 template <int D, int NT>
 __device__ __forceinline__ void store_out(const PrefillArgs& a, const Item& it, int w, int lane,
                                           const SoftmaxAcc<D, NT>& sa) {
-  const int qc = lane & 15, quad = lane >> 4, G = a.G;
+  // (an opaque copy of the lane index: the per-lane row offsets are computed
+  // here, once per item, instead of being hoisted out of the item loop into
+  // registers held across the key loop -- a spill in the fused-q instance)
+  int lane_o = lane;
+  asm volatile("" : "+v"(lane_o));
+  const int qc = lane_o & 15, quad = lane_o >> 4, G = a.G;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float l = sa.l_run[nt];
