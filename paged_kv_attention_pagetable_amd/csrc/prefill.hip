@@ -11,7 +11,9 @@
 // one item on each SIMD, in lockstep or in an explicit MFMA / softmax
 // ping-pong -- all measured slower.)
 // With the fused prologue, q is normalised and rotated in registers as an
-// item loads it (norm_rope_q).
+// item loads it (norm_rope_q); with two or more query heads per kv head the
+// item's rotary rows are staged in LDS (one kernel instance per source of
+// those rows).
 //
 // Keys advance in 64-key chunks.  Each chunk's K rows and V^T rows are copied
 // from their physical pages straight into LDS with gfx950's global-to-LDS
@@ -43,6 +45,12 @@ namespace pkv {
 namespace {
 
 constexpr int kChunk = 64;                // keys per pipeline step
+
+// s_waitcnt immediate that waits until at most n vector memory operations of
+// this wave are outstanding (n < 64; vmcnt bits [3:0] and [15:14], expcnt and
+// lgkmcnt left at their maxima, i.e. not waited on).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) & 3) << 14; }
+
 constexpr int kStagePages = 2048;         // page ids staged in LDS (>= pages_per_slot, host-checked)
 
 // Waves per workgroup and 16-column MFMA tiles per wave: 4 waves of up to
@@ -267,19 +275,36 @@ __device__ __forceinline__ float quad_sum(float v) {
 // dims 8*quad + 32c + j of its column: the mean of squares is a sum over the
 // column's 4 lanes, and the partner of chunk c (< D/64) is the same lane's
 // chunk c + D/64.  fp32 math, one bf16 rounding (as the operand is used).
-// Inputs of the fused q prologue, loaded right after q so that both
-// latencies overlap.
+// Where the transform takes its rotary rows and norm weights from (one
+// kernel instance each, chosen by the host per call):
+//  Regs: loaded into registers right after q, so that both latencies overlap
+//        (head_dim <= 128, one query head per kv head);
+//  Lds:  the item's rows staged in LDS by stage_rope, the weights in
+//        registers (head_dim <= 128, two or more query heads per kv head);
+//  Load: loaded inside the transform, 16 bytes at a time as they are used
+//        (head_dim >= 256, whose per-lane rows would not fit the registers).
+// (The weights, the same for every item, are still loaded per item: read
+// from LDS inside the transform they cost more than their load beside q.)
+enum class RopeSrc { Regs, Lds, Load };
+// q modes of the kernel: q given rotated, or raw with the fused transform
+constexpr int kQReady = 0, kQRope = 1, kQRopeLds = 2;
+
 template <int D, int NT>
 struct QRope {
-  float cs[NT][D / 64][8], sn[NT][D / 64][8];  // cos / sin of the lane's first-half dims
-  u32x4 w[D / 32];                            // q_norm weights of the lane's dims
+  float cs[NT][D / 64][8], sn[NT][D / 64][8];  // cos / sin of the lane's first-half dims (Regs)
+  u32x4 w[D / 32];                            // q_norm weights of the lane's dims (Regs, Lds)
 };
+
+template <int D, int NT>
+__device__ __forceinline__ void load_rope_w(const PrefillArgs& a, int quad, QRope<D, NT>& qr) {
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) qr.w[c] = load16(a.q_w + 8 * quad + 32 * c);
+}
 
 template <int D, int NT>
 __device__ __forceinline__ void load_rope(const PrefillArgs& a, int quad, const WaveQ<D, NT>& wq,
                                           QRope<D, NT>& qr) {
-#pragma unroll
-  for (int c = 0; c < D / 32; ++c) qr.w[c] = load16(a.q_w + 8 * quad + 32 * c);
+  load_rope_w<D, NT>(a, quad, qr);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     // positions past the table (caller error) read its last row: in bounds
@@ -301,24 +326,95 @@ __device__ __forceinline__ void load_rope(const PrefillArgs& a, int quad, const 
   }
 }
 
-// PRE: the rotary inputs were loaded by load_rope into *qr; otherwise they
-// are loaded here, 16 bytes at a time as they are used.
-template <int D, int NT, bool PRE>
+// Lds: with G query heads per kv head the item's columns share each token's
+// cos / sin rows G ways, and every lane loading its own copies cost ~4 us of
+// the Qwen3 prefill call.  The item's Q token rows (cos rows of tokens
+// 0 .. Q-1, then the sin rows, D/8 16-byte units each: Q*D*4 bytes, at most
+// one tile buffer) go to the second tile buffer, free until the key loop's
+// first copy, with global-to-LDS copies issued beside q.  Unit u of token i
+// sits at slot u ^ (i % (D/8)), so the reads of one dim group across tokens
+// spread over the banks.
+template <int D>
+constexpr bool rope_stageable(int q_tokens) {
+  return D <= 128 && q_tokens * D * 4 <= tile_bytes<D>();
+}
+
+template <int D>
+__device__ __forceinline__ int rope_pos(const PrefillArgs& a, const Item& it, int i) {
+  const int p = (i < it.nq && !it.idle) ? it.sp + it.i0 + i : 0;
+  return min(p, a.max_pos - 1);  // positions past the table read its last row: in bounds
+}
+
+template <int D>
+__device__ __forceinline__ void stage_rope(const PrefillArgs& a, const Item& it, uint8_t* buf, int lane, int w) {
+  constexpr int U = D / 8;                   // 16-byte units per row
+  const int Q = a.q_tokens, units = 2 * U * Q;
+  const int n_copies = (units + 63) / 64;    // 1 KB each
+  for (int k = w; k < n_copies; k += prefill_waves<D>()) {
+    const int g = 64 * k + lane;
+    const float* src = a.cos_t;  // (units past the rows: any in-bounds address)
+    if (g < units) {
+      const int tab = g / (U * Q), rem = g - tab * (U * Q), i = rem / U, slot = rem - i * U;
+      const int unit = slot ^ (i % U);
+      src = (tab ? a.sin_t : a.cos_t) + (size_t)rope_pos<D>(a, it, i) * (D / 2) + 4 * unit;
+    }
+    __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(buf + 1024 * k), 16, 0, 0);
+  }
+}
+
+template <int D, int NT, RopeSrc SRC>
 __device__ __forceinline__ void norm_rope_q(const PrefillArgs& a, int quad,
-                                            const QRope<PRE ? D : 64, NT>* qr, WaveQ<D, NT>& wq) {
+                                            const QRope<SRC == RopeSrc::Load ? 64 : D, NT>* qr,
+                                            WaveQ<D, NT>& wq, const uint8_t* rope_lds, int w,
+                                            int lane) {
   constexpr int C = D / 32;   // 16-byte chunks per lane
   constexpr int H = D / 64;   // chunks in the first half of the dims
-  auto wgt = [&](int c) { return PRE ? qr->w[c] : load16(a.q_w + 8 * quad + 32 * c); };
+  constexpr int U = D / 8;    // 16-byte units of a staged rotary row
+  constexpr bool LDS = SRC == RopeSrc::Lds;
+  auto wgt = [&](int c) {
+    if constexpr (SRC == RopeSrc::Load) return load16(a.q_w + 8 * quad + 32 * c);
+    else return qr->w[c];
+  };
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int pos = min(max(wq.pcol[nt], 0), a.max_pos - 1);
     const float* crow = a.cos_t + (size_t)pos * (D / 2) + 8 * quad;
     const float* srow = a.sin_t + (size_t)pos * (D / 2) + 8 * quad;
+    // Lds: the column's token row i (columns without a query read token 0's
+    // or the last staged row: their operand stays zero)
+    float lcs[LDS ? H : 1][8], lsn[LDS ? H : 1][8];
+    if constexpr (LDS) {
+      // (an opaque lane index: these per-lane offsets are computed here, not
+      // hoisted out of the item loop into registers held across the key loop)
+      int lane_o = lane;
+      asm volatile("" : "+v"(lane_o));
+      const int col = w * NT * 16 + nt * 16 + (lane_o & 15);
+      const int i = min(wq.pcol[nt] < 0 ? 0 : col / a.G, a.q_tokens - 1);
+      const float* ct = reinterpret_cast<const float*>(rope_lds) + (size_t)i * (D / 2);
+      const float* st = ct + (size_t)a.q_tokens * (D / 2);
+#pragma unroll
+      for (int c = 0; c < H; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int unit = (2 * (lane_o >> 4) + 8 * c + h) ^ (i % U);
+          const f32x4 cv = *reinterpret_cast<const f32x4*>(ct + 4 * unit);
+          const f32x4 sv = *reinterpret_cast<const f32x4*>(st + 4 * unit);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lcs[c][4 * h + e] = cv[e];
+            lsn[c][4 * h + e] = sv[e];
+          }
+        }
+    }
     auto csv = [&](int c, int j) {
-      return PRE ? qr->cs[nt][c][j] : crow[32 * c + j];
+      if constexpr (LDS) return lcs[c][j];
+      else if constexpr (SRC == RopeSrc::Regs) return qr->cs[nt][c][j];
+      else return crow[32 * c + j];
     };
     auto snv = [&](int c, int j) {
-      return PRE ? qr->sn[nt][c][j] : srow[32 * c + j];
+      if constexpr (LDS) return lsn[c][j];
+      else if constexpr (SRC == RopeSrc::Regs) return qr->sn[nt][c][j];
+      else return srow[32 * c + j];
     };
     float x[C][8];
     float ss = 0.f;
@@ -659,36 +755,46 @@ __device__ __forceinline__ void store_out(const PrefillArgs& a, const Item& it, 
 // One work item end to end: stage its page ids, stream its key chunks through
 // the two LDS tile buffers (the next chunk's copy in flight while the current
 // one is computed), normalise and store.
-// RQ: q arrives raw and gets the fused Qwen3 norm + rotation (norm_rope_q).
-template <int D, int NT, bool RQ>
+// QM: q arrives rotated (kQReady) or raw, getting the fused Qwen3 norm +
+// rotation (norm_rope_q) with its rotary rows in registers (kQRope) or
+// staged in LDS (kQRopeLds).
+template <int D, int NT, int QM>
 __device__ __forceinline__ void run_item(const PrefillArgs& a, const SeqMeta& sm, int hk, int n, int qb,
-                                         uint8_t* lds,
-                                         int* s_pg, const LaneConst<D>& lc, int tid, int lane,
-                                         int w, float inv_c) {
+                                         uint8_t* lds, int* s_pg, const LaneConst<D>& lc,
+                                         int tid, int lane, int w, float inv_c) {
   const int quad = lane >> 4;
   Item it;
   item_init(a, sm, hk, n, qb, it);
-  // The first key chunk's copies go out first and q (and the rotary inputs)
-  // right behind them: one memory round trip before the key loop.  (The page
-  // ids were staged for the whole sequence; the previous item's loop ended
-  // with a barrier, so both tile buffers are free.)
+  // The first key chunk's copies go out first and q (and the transform's
+  // inputs) right behind them: one memory round trip before the key loop.
+  // (The page ids were staged for the whole sequence; the previous item's
+  // loop ended with a barrier, so both tile buffers are free.)  The transform
+  // cannot run under the chunk's copies instead: the compiler counts no
+  // global-to-LDS copy among the loads in flight, so q's first use waits for
+  // every one of them whatever the order.
   if (it.n_chunks > 0) issue_tile<D>(a, it, s_pg, lds, 0, it.j_start, lc, lane, w);
   WaveQ<D, NT> wq;
   load_q<D, NT>(a, it, w, lane, wq);
-  // head_dim <= 128: the rotary inputs are loaded into registers now;
-  // head_dim 256 holds twice as many per lane and loads them inside the
-  // transform, to stay within the register budget
-  QRope<(RQ && D <= 128) ? D : 64, NT> qr;
-  if constexpr (RQ && D <= 128) load_rope<D, NT>(a, quad, wq, qr);
-  SoftmaxAcc<D, NT> sa;
-  acc_init(sa);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first chunk, q and the rotary inputs have landed
+  constexpr RopeSrc SRC = QM == kQRopeLds ? RopeSrc::Lds : D <= 128 ? RopeSrc::Regs : RopeSrc::Load;
+  QRope<(QM != kQReady && SRC != RopeSrc::Load) ? D : 64, NT> qr;
+  uint8_t* const rope_buf = lds + tile_bytes<D>();  // the second tile buffer
+  if constexpr (QM == kQRope && SRC == RopeSrc::Regs) load_rope<D, NT>(a, quad, wq, qr);
+  if constexpr (QM == kQRopeLds) {
+    stage_rope<D>(a, it, rope_buf, lane, w);
+    load_rope_w<D, NT>(a, quad, qr);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the first chunk, q and the transform's inputs have landed
   __syncthreads();
   mask_q<D, NT>(wq);
-  if constexpr (RQ) {
-    if constexpr (D <= 128) norm_rope_q<D, NT, true>(a, quad, &qr, wq);
-    else norm_rope_q<D, NT, false>(a, quad, nullptr, wq);
+  if constexpr (QM != kQReady) {
+    norm_rope_q<D, NT, SRC>(a, quad, &qr, wq, rope_buf, w, lane);
+    // every wave has read the staged rows before the key loop's copies
+    if constexpr (QM == kQRopeLds) __syncthreads();
   }
+  // (the accumulators start after the q transform, which would otherwise
+  // hold them alongside its own working set)
+  SoftmaxAcc<D, NT> sa;
+  acc_init(sa);
   if (it.n_chunks > 0 && zero_tail<D>(lds, 0, it.j_start, it.kv_hi, tid)) __syncthreads();
   constexpr int NB = prefill_bufs<D>();
   for (int ck = 0; ck < it.n_chunks; ++ck) {
@@ -700,7 +806,7 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, const SeqMeta& sm
       __syncthreads();  // every wave is done with the single buffer
       issue_tile<D>(a, it, s_pg, lds, 0, j0 + kChunk, lc, lane, w);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk's copies have landed
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the next chunk's copies have landed
     __syncthreads();
     if (ck + 1 < it.n_chunks && zero_tail<D>(lds, nbuf, j0 + kChunk, it.kv_hi, tid))
       __syncthreads();
@@ -714,7 +820,7 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, const SeqMeta& sm
 // workgroup whose layer exceeds its sequence's block count exits at once).
 // Grid x = kv head: with n_kv a multiple of 8 the XCDs (every 8th workgroup)
 // each keep their heads' K/V in their own L2.
-template <int D, int NT, bool RQ>
+template <int D, int NT, int QM>
 __global__ __launch_bounds__(prefill_threads<D>())
 __attribute__((amdgpu_waves_per_eu(prefill_wpe<D>(), prefill_wpe<D>())))
 void prefill_kernel(const int32_t* cu_seqlens, const int32_t* slots, const int32_t* start_pos,
@@ -739,7 +845,7 @@ void prefill_kernel(const int32_t* cu_seqlens, const int32_t* slots, const int32
     __syncthreads();
   }
   for (int qb = a.n_qblocks - 1 - (int)blockIdx.z; qb < nblk; qb += a.n_qblocks)
-    run_item<D, NT, RQ>(a, sm, hk, n, qb, lds, s_pg, lc, tid, lane, w, inv_c);
+    run_item<D, NT, QM>(a, sm, hk, n, qb, lds, s_pg, lc, tid, lane, w, inv_c);
 }
 
 // ---------------------------------------------------------------------------
@@ -749,14 +855,12 @@ hipError_t set_lds_limit(K* kernel, int bytes) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-template <int D>
-hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t st) {
+template <int D, int QM>
+hipError_t launch_prefill_qm(const PrefillArgs& a, hipStream_t st) {
   constexpr int NT = prefill_nt<D>();
   const int lds = prefill_bufs<D>() * tile_bytes<D>();
-  static const hipError_t attr0 = set_lds_limit(&prefill_kernel<D, NT, false>, lds);
-  static const hipError_t attr1 = set_lds_limit(&prefill_kernel<D, NT, true>, lds);
-  if (attr0 != hipSuccess) return attr0;
-  if (attr1 != hipSuccess) return attr1;
+  static const hipError_t attr = set_lds_limit(&prefill_kernel<D, NT, QM>, lds);
+  if (attr != hipSuccess) return attr;
   // An XCD hands its workgroups to its 4 shader engines round-robin and
   // dispatches in order, stalling when the next workgroup's engine is full.
   // With an even y extent every layer would send the same sequences to the
@@ -766,13 +870,17 @@ hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t st) {
   // batches).  (A 1-D grid in exact cost order, mapped in-kernel, balanced
   // the engines too but its per-workgroup set-up cost more than it saved.)
   dim3 grid(a.g.n_kv, a.n_seqs | 1, a.n_qblocks);
-  if (a.q_w)
-    hipLaunchKernelGGL((prefill_kernel<D, NT, true>), grid, dim3(prefill_threads<D>()), lds, st,
-                       a.cu_seqlens, a.slots, a.start_pos, a.pt.table, a.n_seqs, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<D, NT, false>), grid, dim3(prefill_threads<D>()), lds, st,
-                       a.cu_seqlens, a.slots, a.start_pos, a.pt.table, a.n_seqs, a);
+  hipLaunchKernelGGL((prefill_kernel<D, NT, QM>), grid, dim3(prefill_threads<D>()), lds, st,
+                     a.cu_seqlens, a.slots, a.start_pos, a.pt.table, a.n_seqs, a);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t st) {
+  if (!a.q_w) return launch_prefill_qm<D, kQReady>(a, st);
+  if constexpr (D <= 128)
+    if (rope_stageable<D>(a.q_tokens)) return launch_prefill_qm<D, kQRopeLds>(a, st);
+  return launch_prefill_qm<D, kQRope>(a, st);
 }
 
 }  // namespace

@@ -187,9 +187,13 @@ def _check_with_prologue(case, kp, vp, table, okp, ovp, name, hint=None):
     assert_attn_close(host_f64(out), ref, name)
 
 
+# The prologue's rotary rows come from registers (one query head per kv head:
+# g1_ps16), from LDS staging (two or more at head_dim <= 128: 2, 3, 4 and 16
+# query heads per kv head, 64 down to 8 tokens per item) or from loads inside
+# the transform (head_dim 256 / 512).
 @pytest.mark.parametrize("name", ["tiny", "d128_g4_ragged", "d128_g4_prefix", "d256_w64",
-                                  "d512_ragged",
-                                  "slot0_pad", "empty_prompts"])
+                                  "d512_ragged", "g1_ps16", "d128_g3", "g16", "kv16_g2",
+                                  "d64_w100_prefix", "slot0_pad", "empty_prompts"])
 def test_prefill_with_prologue_matches_oracle(name):
     case = _case(name, seed=7)
     kp, vp, table, okp, ovp = _pools_with_prefix(case)
