@@ -484,10 +484,12 @@ PMC_PARTS = {
     "decode_llama_decode": (("decode_keysplit_kernel<128, 4>",), DECODE_SRC),
     "decode_qwen3_decode": (("decode_keysplit_kernel<128, 8>",), DECODE_SRC),
     "decode_gemma_mixed": (("decode_dimsplit_kernel<",), DECODE_SRC),
-    # prefill attention without the q transform (keys appended beforehand)
-    "prefill_qwen3_prefill": (("prefill_kernel<", ", false>"), PREFILL_SRC),
-    # prefill attention with the fused q norm + RoPE
-    "prefill_fused_q_qwen3_prefill": (("prefill_kernel<", ", true>"), PREFILL_SRC),
+    # prefill attention without the q transform (keys appended beforehand):
+    # the instance of q mode 0
+    "prefill_qwen3_prefill": (("prefill_kernel<", ", 0>"), PREFILL_SRC),
+    # prefill attention with the fused q norm + RoPE: with 4 query heads per
+    # kv head, the instance whose rotary rows are staged in LDS (q mode 2)
+    "prefill_fused_q_qwen3_prefill": (("prefill_kernel<", ", 2>"), PREFILL_SRC),
 }
 
 
@@ -546,7 +548,7 @@ def summarize_mfma(db_path, out_path, command=""):
     MFMA FLOPs executed vs algorithmic."""
     import sqlite3
     db = sqlite3.connect(db_path)
-    key = "%prefill_kernel<%, false>%"
+    key = "%prefill_kernel<%, 0>%"
     vals = {}
     for c in MFMA_COUNTERS:
         rows = db.execute("select dispatch_id, sum(counter_value) from pmc_events where name like ? "
@@ -564,7 +566,7 @@ def summarize_mfma(db_path, out_path, command=""):
         pass
     gui = vals.get("GRBM_GUI_ACTIVE")
     busy = vals.get("SQ_VALU_MFMA_BUSY_CYCLES")
-    rec = dict(kernel="prefill_kernel<128, 2, false> (qwen3_prefill attention)",
+    rec = dict(kernel="prefill_kernel<128, 2, 0> (qwen3_prefill attention)",
                source_sha=source_sha(PREFILL_SRC), counters=vals,
                kernel_ns_under_counters=dur_ns, command=command)
     if gui and busy:
