@@ -26,6 +26,11 @@ CASES = {
     "w1": (4, 2, 64, 16, [37, 50], 1, None),
     "d128_ps256": (16, 4, 128, 256, [700, 255, 256, 257, 1, 0, 2000], 0, None),
     "all_idle": (32, 8, 128, 128, [0, 0, 0], 0, None),
+    # one long row of many splits beside short one-split rows, with idle rows
+    # among them
+    "long_among_short": (32, 8, 128, 64, [4000] + [3, 40, 0, 65, 1, 33, 0] * 4, 0, None),
+    # many short rows (80 rows, one split each)
+    "many_short": (8, 2, 64, 16, [int(x) for x in np.arange(1, 81) * 7 % 97], 0, None),
 }
 
 
