@@ -10,8 +10,11 @@ then attends (+ the in-kernel log-sum-exp merge).  This is the largest
 single-GPU decode configuration; it gives the JSON line's ``value`` and
 ``roofline``.  The other decode workloads -- ``qwen3_decode`` (8 rows of a
 Qwen3-4B step, 36 layers) and ``gemma_mixed`` (64 rows, one Gemma-4 sliding
-head_dim-256 and one full head_dim-512 layer per step) -- are reported under
-``extra_decode`` with their own rooflines, and the Qwen3-4B chunked prefill
+head_dim-256 and one full head_dim-512 layer per step) and
+``llama_decode_tp8_share`` (one GPU's share of the Llama step under 8-way
+tensor parallelism: 3 query heads over 1 kv head, the same rows; its kernel
+instance is the Qwen3 one, so no counter traffic is attributed to it) -- are
+reported under ``extra_decode`` with their own rooflines, and the Qwen3-4B chunked prefill
 (16 prompts U[32, 512], fused q/k RMSNorm + RoPE + append prologue, then MFMA
 prefill attention, 36 layers) under ``prefill``.
 
@@ -854,8 +857,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-tp8-share", action="store_true",
+                    help="leave out the llama_decode_tp8_share line (profiler runs: its kernel "
+                         "instance is the Qwen3 one, whose per-dispatch figures it would mix)")
     ap.add_argument("--workload", default="llama_decode",
-                    choices=["llama_decode", "qwen3_decode", "gemma_mixed"],
+                    choices=["llama_decode", "qwen3_decode", "gemma_mixed",
+                             "llama_decode_tp8_share"],
                     help="the decode workload of the headline line (default: the largest)")
     ap.add_argument("--no-extra-decode", action="store_true",
                     help="skip the other decode workloads")
@@ -921,7 +928,10 @@ def main():
             result[k] = head[k]
     if not args.no_extra_decode:
         result["extra_decode"] = {}
-        for name in ("qwen3_decode", "llama_decode", "gemma_mixed"):
+        names = ["qwen3_decode", "llama_decode", "gemma_mixed"]
+        if not args.no_tp8_share:
+            names.append("llama_decode_tp8_share")
+        for name in names:
             if name != args.workload:
                 result["extra_decode"][name] = decode_record(name, args)
     if args.calibrate_copy:

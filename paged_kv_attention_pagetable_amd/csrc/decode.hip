@@ -838,6 +838,14 @@ DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_h
           ((range + split - 1) / split) * G > kMaxMergeUnits) &&
          split < (1 << 24))
     split *= 2;
+  // Key split (head_dim <= 128): four 32-key chunks per wave, i.e. 512-key
+  // splits over 4 waves, whenever that still gives at least one workgroup per
+  // CU -- fewer workgroups than the budget above allows, so fewer set-ups and
+  // partials to merge.  Measured on one GPU's share of the Llama shape under
+  // 8-way tensor parallelism (64 rows, 3 query / 1 kv head): 21.5 us, against
+  // 24.1 / 26.7 / 40.6 with 256- / 1024- / 2048-key splits and 34.4 with the
+  // 8-wave short splits below; the full Llama shape already plans 512.
+  if (head_dim <= 128 && split < 512 && pairs * ((range + 511) / 512) >= 256) split = 512;
   // Short splits: when every wave of a 4-wave workgroup would get a single
   // 32-key chunk, 8-wave workgroups over 256-key splits (half the workgroups,
   // half the partials to merge) measured faster: Qwen3 shape 10.9 -> 10.2 us.

@@ -21,6 +21,11 @@ CONFIGS = {
     "llama_decode": dict(index=2, n_q=24, n_kv=8, head_dim=128, page_size=128, B=64,
                          max_slots=65, len_lo=128, len_hi=4096, idle_frac=0.10, window=0,
                          layers=2),
+    # one GPU's share of llama_decode under 8-way tensor parallelism (kv heads
+    # split across GPUs): 3 query heads over 1 kv head, the same rows and lengths
+    "llama_decode_tp8_share": dict(index=2, n_q=3, n_kv=1, head_dim=128, page_size=128, B=64,
+                                   max_slots=65, len_lo=128, len_hi=4096, idle_frac=0.10,
+                                   window=0, layers=2),
     "qwen3_prefill": dict(index=3, n_q=32, n_kv=8, head_dim=128, page_size=128,
                           n_seqs=16, max_slots=17, len_lo=32, len_hi=512, eps=1e-6,
                           theta=1e6, layers=36),
@@ -289,7 +294,7 @@ def config_lengths(name: str, salt: int = 0):
     if name in ("qwen3_decode",):
         L = rng.integers(c["len_lo"], c["len_hi"] + 1, size=c["B"]).astype(np.int32)
         return L, np.arange(1, c["B"] + 1, dtype=np.int32)
-    if name == "llama_decode":
+    if name in ("llama_decode", "llama_decode_tp8_share"):
         B = c["B"]
         L = rng.integers(c["len_lo"], c["len_hi"] + 1, size=B).astype(np.int32)
         idle = rng.choice(B, size=int(round(c["idle_frac"] * B)), replace=False)

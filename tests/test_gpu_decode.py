@@ -280,6 +280,13 @@ def test_full_llama_decode_all_rows():
     _full_check(case, hint)
 
 
+def test_full_llama_tp8_share_all_rows():
+    """One GPU's share of the Llama call under 8-way tensor parallelism."""
+    case, hint = _full_case("llama_decode_tp8_share")
+    assert (case.seq_lens == 0).sum() == 6 and case.n_q == 3 and case.n_kv == 1
+    _full_check(case, hint)
+
+
 def test_full_gemma_sliding_layer_all_rows():
     c = CONFIGS["gemma_mixed"]
     case, hint = _full_case("gemma_mixed", layer_dim=c["sliding_dim"], window=c["window"])
