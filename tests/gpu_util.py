@@ -43,6 +43,16 @@ def assert_attn_close(gpu: np.ndarray, ref: np.ndarray, what: str = ""):
     return mx
 
 
+def bf16_ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """Distance in bf16 units in the last place between two arrays of bf16 bit
+    patterns (finite values): the bits mapped to integers in the order of the
+    values they encode (negatives mirrored below zero), then subtracted."""
+    def key(u):
+        u = u.astype(np.int64)
+        return np.where(u < 0x8000, u, 0x8000 - u)
+    return np.abs(key(a_bits) - key(b_bits))
+
+
 def gpu_pools(case):
     kp, vp = pkv.new_pools(case.n_pages, case.n_kv, case.page_size, case.head_dim, DEV,
                            fill=int(SENTINEL_BITS.astype(np.int16)))

@@ -7,8 +7,8 @@ import torch
 import oracle
 import paged_kv_attention_pagetable_amd as pkv
 from synth import CONFIGS, config_lengths, make_prefill_case
-from tests.gpu_util import (DEV, assert_attn_close, dev_bits, dev_i32, gpu_pools, host_bits,
-                            host_f64)
+from tests.gpu_util import (DEV, assert_attn_close, bf16_ulp_distance, dev_bits, dev_i32,
+                            gpu_pools, host_bits, host_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -170,6 +170,8 @@ def _check_with_prologue(case, kp, vp, table, okp, ovp, name, hint=None):
     assert_attn_close(oracle.bf16_bits_to_f64(gq[live]), q2[live], "q'")
     ulp_ok = np.mean(gq[live] == q2b[live])
     assert ulp_ok >= 0.99, f"only {ulp_ok:.4f} of q' match the RNE-rounded fp64 value"
+    near = np.mean(bf16_ulp_distance(gq[live], q2b[live]) <= 1)
+    assert near >= 0.999, f"only {near:.5f} of q' within 1 bf16 ulp of the RNE-rounded fp64 value"
     assert np.all(gq[~live] == 0xFFFF), "q' written for a padding sequence"
     # the K pool holds k' (within tolerance of the fp64 value, and almost
     # always its nearest bf16), the V pool the raw v bit for bit
@@ -181,6 +183,8 @@ def _check_with_prologue(case, kp, vp, table, okp, ovp, name, hint=None):
     assert np.max(np.abs(kd)) <= 2e-2
     ulp_ok = np.mean(gk[written] == okb[written])
     assert ulp_ok >= 0.99, f"only {ulp_ok:.4f} of k' match the RNE-rounded fp64 value"
+    near = np.mean(bf16_ulp_distance(gk[written], okb[written]) <= 1)
+    assert near >= 0.999, f"only {near:.5f} of k' within 1 bf16 ulp of the RNE-rounded fp64 value"
     assert np.array_equal(host_bits(vp), ovp)
     ref, _ = oracle.attn_prefill(q2b, okp, ovp, case.table, case.cu_seqlens, case.slots,
                                  case.start_pos, case.scale, case.window)
