@@ -278,58 +278,88 @@ __device__ __forceinline__ uint64_t load_dev2(const float* p) {  // p 8-byte ali
 
 // Log-sum-exp merge of the n_valid split partials of one (row, kv head), in
 // fixed split order (bitwise deterministic whichever workgroup merges).  One
-// pass: each thread owns two output dims of one query head and issues the
-// (max, sum) pair and the partial o of up to kU splits together, merging them
-// online against a running maximum, so the whole merge costs one memory round
-// trip per kU splits.
-template <int D>
-__device__ void merge_splits(const DecodeArgs& a, int b, int hk, int n_valid) {
+// pass: each thread owns P consecutive output dim pairs of one query head
+// (P = G*D/2 over the threads, see merge_splits) and issues the (max, sum) pair
+// and the partial o of all of them for up to kU splits together, merging
+// them online against a running maximum, so the whole merge costs one memory
+// round trip per kU splits.  (One pair per thread at a time made the
+// head_dim-512 merge four dependent round trips per kU splits.)
+template <int D, int P>
+__device__ void merge_splits_p(const DecodeArgs& a, int b, int hk, int n_valid) {
   const int G = a.G, S = a.max_splits;
   const size_t pbase = ((size_t)b * a.g.n_kv + hk) * S;
-  const float* ml = a.part_ml + pbase * G * 2;
   constexpr int kU = 8;  // splits whose loads are in flight together
-  for (int idx = threadIdx.x; idx < G * D / 2; idx += blockDim.x) {
-    const int g = (2 * idx) / D, d = 2 * idx - g * D;
-    const float* po = a.part_o + (pbase * G + g) * D + d;
-    float M = -INFINITY, lsum = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int t0 = 0; t0 < n_valid; t0 += kU) {
-      uint64_t v[kU], w[kU];
+  constexpr int kMaxP = P;
+  const int npairs = G * D / 2;
+  const int p0 = (int)threadIdx.x * P;
+  if (p0 >= npairs) return;  // (no barrier follows)
+  const int g = (2 * p0) / D, d0 = 2 * p0 - g * D;
+  const float* ml = a.part_ml + (pbase * G + g) * 2;
+  const float* po = a.part_o + (pbase * G + g) * D + d0;
+  float M = -INFINITY, lsum = 0.f;
+  float o[kMaxP][2];
 #pragma unroll
-      for (int j = 0; j < kU; ++j) {
-        const bool ok = t0 + j < n_valid;
-        v[j] = ok ? load_dev2(po + (size_t)(t0 + j) * G * D) : 0;
-        w[j] = ok ? load_dev2(ml + ((t0 + j) * G + g) * 2) : 0;
+  for (int i = 0; i < kMaxP; ++i) o[i][0] = o[i][1] = 0.f;
+  for (int t0 = 0; t0 < n_valid; t0 += kU) {
+    uint64_t v[kMaxP][kU], w[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const bool ok = t0 + j < n_valid;
+      w[j] = ok ? load_dev2(ml + (size_t)(t0 + j) * G * 2) : 0;
+#pragma unroll
+      for (int i = 0; i < kMaxP; ++i) v[i][j] = ok ? load_dev2(po + (size_t)(t0 + j) * G * D + 2 * i) : 0;
+    }
+    // A split's (max, sum) is (m, l); l == 0 marks an empty partial, whose
+    // o was never written: it is selected away, never multiplied.
+    float mg = M;
+#pragma unroll
+    for (int j = 0; j < kU; ++j)
+      if (__uint_as_float((uint32_t)(w[j] >> 32)) > 0.f) mg = fmaxf(mg, __uint_as_float((uint32_t)w[j]));
+    if (mg > M) {
+      const float alpha = fast_exp2(M - mg);  // 0 while M is -inf
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < kMaxP; ++i) {
+        o[i][0] *= alpha;
+        o[i][1] *= alpha;
       }
-      // A split's (max, sum) is (m, l); l == 0 marks an empty partial, whose
-      // o was never written: it is selected away, never multiplied.
-      float mg = M;
+      M = mg;
+    }
 #pragma unroll
-      for (int j = 0; j < kU; ++j)
-        if (__uint_as_float((uint32_t)(w[j] >> 32)) > 0.f) mg = fmaxf(mg, __uint_as_float((uint32_t)w[j]));
-      if (mg > M) {
-        const float alpha = fast_exp2(M - mg);  // 0 while M is -inf
-        lsum *= alpha;
-        o0 *= alpha;
-        o1 *= alpha;
-        M = mg;
-      }
+    for (int j = 0; j < kU; ++j) {
+      const float l = __uint_as_float((uint32_t)(w[j] >> 32));
+      if (l > 0.f) {
+        const float f = fast_exp2(__uint_as_float((uint32_t)w[j]) - M);
+        lsum += f * l;
 #pragma unroll
-      for (int j = 0; j < kU; ++j) {
-        const float l = __uint_as_float((uint32_t)(w[j] >> 32));
-        if (l > 0.f) {
-          const float f = fast_exp2(__uint_as_float((uint32_t)w[j]) - M);
-          lsum += f * l;
-          o0 += f * __uint_as_float((uint32_t)v[j]);
-          o1 += f * __uint_as_float((uint32_t)(v[j] >> 32));
+        for (int i = 0; i < kMaxP; ++i) {
+          o[i][0] += f * __uint_as_float((uint32_t)v[i][j]);
+          o[i][1] += f * __uint_as_float((uint32_t)(v[i][j] >> 32));
         }
       }
     }
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    a.out[((size_t)b * a.n_q + hk * G + g) * D + d] = f32_to_bf16(o0 * inv);
-    a.out[((size_t)b * a.n_q + hk * G + g) * D + d + 1] = f32_to_bf16(o1 * inv);
-    if (a.lse && d == 0)
-      a.lse[(size_t)b * a.n_q + hk * G + g] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
   }
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  bf16_t* orow = a.out + ((size_t)b * a.n_q + hk * G + g) * D + d0;
+#pragma unroll
+  for (int i = 0; i < kMaxP; ++i)
+    *reinterpret_cast<uint32_t*>(orow + 2 * i) = pack_bf16x2(o[i][0] * inv, o[i][1] * inv);
+  if (a.lse && d0 == 0)
+    a.lse[(size_t)b * a.n_q + hk * G + g] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
+}
+
+// P: the smallest power of two with P * threads >= G*D/2 (1, 2 or 4, as
+// G * D <= 2048 and the workgroups have 256 or 512 threads; a divisor of D/2,
+// so a thread's pairs lie in one head).
+template <int D>
+__device__ void merge_splits(const DecodeArgs& a, int b, int hk, int n_valid) {
+  const int npairs = a.G * D / 2;
+  if (npairs <= (int)blockDim.x)
+    merge_splits_p<D, 1>(a, b, hk, n_valid);
+  else if (npairs <= 2 * (int)blockDim.x)
+    merge_splits_p<D, 2>(a, b, hk, n_valid);
+  else
+    merge_splits_p<D, 4>(a, b, hk, n_valid);
 }
 
 // Writes this workgroup's result: the final output when it is the row's only

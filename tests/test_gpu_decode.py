@@ -21,6 +21,9 @@ CASES = {
     "d128_ps16": (8, 2, 128, 16, [300, 17, 16, 1000], 0, None),
     "d256_w512": (8, 2, 256, 64, [256, 511, 512, 513, 1536, 900], 512, None),
     "d512_full": (8, 2, 512, 64, [256, 1536, 777], 0, None),
+    # G * head_dim = 1536: the merge's 768 dim pairs take 4 per thread (a
+    # power of two, so a thread's pairs stay inside one query head)
+    "d512_g3": (6, 2, 512, 64, [700, 1536, 33, 1100], 0, None),
     "g1": (8, 8, 128, 128, [500, 1], 0, None),
     "g16": (16, 1, 64, 32, [200, 33], 0, None),
     "w1": (4, 2, 64, 16, [37, 50], 1, None),
