@@ -177,10 +177,13 @@ pkv_status pkv_append(const void* k_new, const void* v_new, const int32_t* slot,
  *              workspace once when it is created (before its first call,
  *              outside any graph capture); every call leaves its counters at
  *              zero again.  The counters are addressed back from
- *              workspace + workspace_bytes, so a workspace reused by calls of
- *              different shapes must be passed with the same workspace_bytes
- *              each time.  Calls that overlap in time (other streams, other
- *              graphs) need separate workspaces; calls with separate
+ *              workspace + workspace_bytes, and whatever the call's shape
+ *              they lie in the workspace's last (workspace_bytes / 16,
+ *              rounded down to 16) bytes, which no call's partials reach:
+ *              calls of different shapes may share a workspace, passed with
+ *              the same workspace_bytes each time and at least the size each
+ *              of them needs.  Calls that overlap in time (other streams,
+ *              other graphs) need separate workspaces; calls with separate
  *              workspaces share nothing.
  * n_q_heads / n_kv_heads must be an integer G in [1, 16] with G * head_dim <= 2048
  * (PKV_ERR_UNSUPPORTED otherwise).  B == 0 is a no-op.
@@ -222,7 +225,8 @@ pkv_status pkv_attn_decode_noalloc(const void* q, int32_t n_q_heads, const int32
                                    int32_t window, void* out, float* lse, void* stream);
 
 /* Bytes of workspace pkv_attn_decode needs for these sizes (0 = none): the
- * split partials plus 4 * B * n_kv_heads bytes of arrival counters. */
+ * split partials, and a last sixteenth (at least 4 * B * n_kv_heads bytes) for
+ * the arrival counters that the partials of no call reach. */
 size_t pkv_decode_workspace_size(int32_t B, int32_t n_q_heads, int32_t n_kv_heads,
                                  int32_t head_dim, int32_t max_seq_len_hint,
                                  int32_t window);

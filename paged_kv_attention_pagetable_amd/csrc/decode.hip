@@ -39,6 +39,7 @@
 // zero on the last arrival -- no release fence, which on gfx950 would write
 // back the whole L2 per workgroup (see finish).  Optionally the new token's
 // K/V is appended first by the workgroup that owns the last key.
+#include <algorithm>
 #include <mutex>
 
 #include "pkv_device.h"
@@ -899,10 +900,17 @@ DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_h
   }
   const size_t units = (size_t)B * n_kv * p.max_splits * G;
   p.part_o_floats = (units * head_dim + 63) & ~(size_t)63;
-  // partials from the start, then the (row, kv head) arrival counters, which
-  // the kernel addresses back from the workspace's end
-  p.ws_bytes = ((p.part_o_floats + units * 2) * sizeof(float) + (size_t)B * n_kv * 4 + 15) &
-               ~(size_t)15;
+  // partials from the start, then (at the end, in the workspace's counter
+  // region) the (row, kv head) arrival counters, which the kernel addresses
+  // back from the workspace's end.  The size makes the region hold this
+  // call's counters and keeps the partials below it, with room to spare, for
+  // this size and every larger one.
+  const size_t part = (p.part_o_floats + units * 2) * sizeof(float);
+  const size_t ctr = (size_t)B * n_kv * 4;
+  size_t ws = std::max(16 * ctr, part + part / 15 + 16);
+  ws = (ws + 255) & ~(size_t)255;
+  while (part + 16 > ws - ws / 16 || ctr > decode_counter_region(ws)) ws += 256;
+  p.ws_bytes = ws;
   return p;
 }
 

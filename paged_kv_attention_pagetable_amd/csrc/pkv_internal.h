@@ -178,6 +178,13 @@ struct DecodePlan {
 DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_hint,
                        int window);
 
+// A decode workspace of ws bytes keeps its last decode_counter_region(ws)
+// bytes for the arrival counters of every call that uses it, whatever that
+// call's shape; the split partials stay below that region.  (With counters
+// simply after each call's own partials, a call of another shape could write
+// partials over counters that a later call relies on being zero.)
+inline size_t decode_counter_region(size_t ws) { return (ws / 16) & ~(size_t)15; }
+
 // Static split-K scratch of pkv_attn_decode_noalloc: one buffer of this many
 // bytes per device, inside the library's code object.  decode_scratch gives
 // the current device's copy (its address is looked up once per device).

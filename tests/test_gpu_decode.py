@@ -128,6 +128,37 @@ def test_decode_workspace_reused_across_calls_and_shapes():
         assert_attn_close(host_f64(out), ref, f"reuse {seed}")
 
 
+def test_decode_two_shapes_share_one_workspace():
+    """Calls of two shapes alternate on one workspace sized for both: one with
+    few (row, kv head) pairs whose long rows fill the partials up to the top
+    of its plan (4 rows, G 16, rows of 64k keys in 64 splits), one with many
+    pairs and their counters (64 rows x 8 kv heads, two splits per row).  The
+    first call's partials must not reach the counters the second relies on
+    being zero: every call matches the oracle and leaves the counters at 0."""
+    big = make_decode_case(16, 1, 128, 128, [65536, 100, 65535, 65536], max_slots=6, seed=2101,
+                           spare_pages=2)
+    rng = np.random.default_rng(2102)
+    many = make_decode_case(32, 8, 64, 16, [int(x) for x in rng.integers(600, 1025, size=64)],
+                            max_slots=66, seed=2103, spare_pages=2)
+    hints = {id(big): 65536, id(many): 1024}
+    need = [pkv.decode_workspace_size(c.B, c.n_q, c.n_kv, c.head_dim, hints[id(c)])
+            for c in (big, many)]
+    assert min(need) > 0 and need[0] > need[1]
+    ws = pkv.new_decode_workspace(max(need), DEV)
+    runs = []
+    for c in (big, many):
+        kp, vp, table = gpu_decode_setup(c)
+        okp, ovp = oracle_decode_pools(c)
+        ref, _ = oracle.attn_decode(c.q, okp, ovp, c.table, c.slots, c.seq_lens, c.scale, 0)
+        runs.append((c, kp, vp, table, ref))
+    region = (ws.numel() // 16) // 16 * 16          # the counters' bytes at the end
+    for it in range(2):
+        for c, kp, vp, table, ref in runs:
+            out, _ = run_gpu_decode(c, kp, vp, table, hint=hints[id(c)], workspace=ws)
+            assert_attn_close(host_f64(out), ref, f"shape B={c.B} call {it}")
+            assert int(ws[-region:].count_nonzero()) == 0
+
+
 def test_decode_fused_append_past_capacity_is_skipped():
     """A row whose length exceeds its slot's table (a caller error): the fused
     append must skip its new token, as pkv_append does, and leave the cached
