@@ -13,7 +13,8 @@ Qwen3-4B step, 36 layers) and ``gemma_mixed`` (64 rows, one Gemma-4 sliding
 head_dim-256 and one full head_dim-512 layer per step) and
 ``llama_decode_tp8_share`` (one GPU's share of the Llama step under 8-way
 tensor parallelism: 3 query heads over 1 kv head, the same rows; its kernel
-instance is the Qwen3 one, so no counter traffic is attributed to it) -- are
+instance is also the Llama step's, so its counter traffic comes from a run of
+it alone) -- are
 reported under ``extra_decode`` with their own rooflines, and the Qwen3-4B chunked prefill
 (16 prompts U[32, 512], fused q/k RMSNorm + RoPE + append prologue, then MFMA
 prefill attention, 36 layers) under ``prefill``.
@@ -419,7 +420,7 @@ def _pmc_record(part):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha") != source_sha(PMC_PARTS[part][1]):
+    if rec.get("source_sha") != source_sha({**PMC_PARTS, **PMC_SOLO_PARTS}[part][1]):
         return None   # kernel changed since the counters were taken
     return rec
 
@@ -494,14 +495,23 @@ PMC_PARTS = {
     # kv head, the instance whose rotary rows are staged in LDS (q mode 2)
     "prefill_fused_q_qwen3_prefill": (("prefill_kernel<", ", 2>"), PREFILL_SRC),
 }
+# Parts whose kernel instance another workload runs too: summarized only from
+# a counter run of that workload alone (``--pmc-parts``; bench.py
+# --workload <name> --no-extra-decode --no-prefill).
+PMC_SOLO_PARTS = {
+    # one GPU's share of the Llama step at 8-way tensor parallelism: a
+    # head_dim-128 key split like the Llama and Qwen3 calls
+    "decode_llama_decode_tp8_share": (("decode_keysplit_kernel<128, ",), DECODE_SRC),
+}
 
 
-def summarize_pmc(fetch_db, write_db, out_dir, command=""):
+def summarize_pmc(fetch_db, write_db, out_dir, command="", only=None):
     """HBM bytes per call of every part's kernel(s) = FETCH_SIZE + WRITE_SIZE (KiB
     per dispatch), each scaled by what the counter reads for a 256 MiB device
     copy (``--calibrate-copy``): one ``<part>_pmc.json`` per part whose kernels
     ran.  Per call = the counted dispatches' bytes over their number.  Other
-    library kernels of the run are listed for reference."""
+    library kernels of the run are listed for reference.  ``only``: the names
+    of the parts to summarize (the solo parts are summarized only when named)."""
     fetch = _pmc_per_kernel(fetch_db, "FETCH_SIZE")
     write = _pmc_per_kernel(write_db, "WRITE_SIZE")
     copy_bytes = 128 * 2**20 * 2
@@ -511,7 +521,10 @@ def summarize_pmc(fetch_db, write_db, out_dir, command=""):
         return copy_bytes / (max(vals) * 1024.0) if vals else None
 
     f_scale, w_scale = copy_scale(fetch), copy_scale(write)
-    for part, (key, sources) in PMC_PARTS.items():
+    table = {**PMC_PARTS, **PMC_SOLO_PARTS} if only else PMC_PARTS
+    for part, (key, sources) in table.items():
+        if only and part not in only:
+            continue
         total, n = 0.0, 0
         parts = {}
         for k in sorted(set(fetch) | set(write)):
@@ -859,7 +872,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-tp8-share", action="store_true",
                     help="leave out the llama_decode_tp8_share line (profiler runs: its kernel "
-                         "instance is the Qwen3 one, whose per-dispatch figures it would mix)")
+                         "instance is also the Llama step's, whose per-dispatch figures it would "
+                         "mix)")
     ap.add_argument("--workload", default="llama_decode",
                     choices=["llama_decode", "qwen3_decode", "gemma_mixed",
                              "llama_decode_tp8_share"],
@@ -882,6 +896,9 @@ def main():
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DB", "OUT"),
                     help="write a kernel-duration summary of a rocprofv3 database and exit")
+    ap.add_argument("--pmc-parts", default="",
+                    help="with --summarize-pmc: comma-separated parts to summarize (default: "
+                         "every part of a full bench run; the solo parts only when named)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "OUT_DIR"),
                     help="write HBM traffic per call of every part's kernels from two "
                          "rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) and exit")
@@ -897,7 +914,8 @@ def main():
         summarize_mfma(*args.summarize_mfma, command=args.command)
         return
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc, command=args.command)
+        summarize_pmc(*args.summarize_pmc, command=args.command,
+                      only=args.pmc_parts.split(",") if args.pmc_parts else None)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this bench runs the single-GPU path only; "
