@@ -24,6 +24,7 @@ CASES = {
     "d512_ragged": (8, 2, 512, 64, [70, 1, 130], None, 0),
     "d512_prefix_w40_ps16": (16, 4, 512, 16, [50, 33], [20, 0], 40),
     "g1_ps16": (4, 4, 128, 16, [90, 31], None, 0),
+    "g1_d64": (4, 4, 64, 32, [70, 33, 129], [0, 5, 0], 0),
     "g16": (16, 1, 64, 32, [40, 9], None, 0),
     "kv16_g2": (32, 16, 64, 32, [40, 90, 7], None, 0),
     "kv3_g4": (12, 3, 128, 64, [70, 130], [0, 9], 0),
@@ -192,11 +193,11 @@ def _check_with_prologue(case, kp, vp, table, okp, ovp, name, hint=None):
 
 
 # The prologue's rotary rows come from registers (one query head per kv head:
-# g1_ps16), from LDS staging (two or more at head_dim <= 128: 2, 3, 4 and 16
+# g1_ps16, g1_d64), from LDS staging (two or more at head_dim <= 128: 2, 3, 4 and 16
 # query heads per kv head, 64 down to 8 tokens per item) or from loads inside
 # the transform (head_dim 256 / 512).
 @pytest.mark.parametrize("name", ["tiny", "d128_g4_ragged", "d128_g4_prefix", "d256_w64",
-                                  "d512_ragged", "g1_ps16", "d128_g3", "g16", "kv16_g2",
+                                  "d512_ragged", "g1_ps16", "g1_d64", "d128_g3", "g16", "kv16_g2",
                                   "d64_w100_prefix", "slot0_pad", "empty_prompts"])
 def test_prefill_with_prologue_matches_oracle(name):
     case = _case(name, seed=7)
