@@ -327,8 +327,9 @@ __device__ __forceinline__ void load_rope(const PrefillArgs& a, int quad, const 
 }
 
 // Lds: with G query heads per kv head the item's columns share each token's
-// cos / sin rows G ways, and every lane loading its own copies cost ~4 us of
-// the Qwen3 prefill call.  The item's Q token rows (cos rows of tokens
+// cos / sin rows G ways; staged once per item instead of loaded by every lane
+// (G-fold redundant), they measured 0.45 us less per Qwen3 prefill call
+// (48.27 -> 47.80 us).  The item's Q token rows (cos rows of tokens
 // 0 .. Q-1, then the sin rows, D/8 16-byte units each: Q*D*4 bytes, at most
 // one tile buffer) go to the second tile buffer, free until the key loop's
 // first copy, with global-to-LDS copies issued beside q.  Unit u of token i
