@@ -826,6 +826,16 @@ def prefill_record(args):
     ms_fq = time_graph(gp_fq, args.kernel_reps, 2) / pw.n_calls
     fl = pw.flops_per_call()
     ab = pw.attn_bytes()
+    # Reference stream: a plain device copy of each layer's q into its out
+    # buffer (the q read and out write every attention call makes, 81.7 MB),
+    # timed the same way -- what the compulsory q / out traffic alone takes.
+    def copy_q_out():
+        for ly in pw.layers:
+            ly["out"].copy_(ly["q"])
+    gp_copy = capture(copy_q_out)
+    ms_copy = time_graph(gp_copy, args.kernel_reps, 2) / pw.n_calls
+    copy_bytes = 2 * pw.layers[0]["q"].numel() * pw.layers[0]["q"].element_size()
+    del gp_copy
 
     def roof(ms, part, kernel):
         tf = fl / (ms * 1e-3) / 1e12
@@ -856,6 +866,10 @@ def prefill_record(args):
             algorithmic_bytes_per_call=ab, us_per_call=round(ms_pa * 1e3, 3),
             arithmetic_intensity=round(fl / ab, 1),
             ridge=round(MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9), 1)),
+        "q_out_copy_reference": dict(
+            us_per_call=round(ms_copy * 1e3, 3), bytes_per_call=copy_bytes,
+            achieved=round(copy_bytes / (ms_copy * 1e-3) / 1e9, 1), unit="GB/s",
+            kernel="torch copy_ of q into out (the attention's compulsory q / out traffic)"),
         "prologue_us_per_call": round((ms_p / pw.n_calls - ms_fq) * 1e3, 3),
         "prologue_bytes_per_call": pw.prologue_bytes(),
     }
