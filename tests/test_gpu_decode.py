@@ -20,6 +20,9 @@ CASES = {
     "d128_g3_ps64": (24, 8, 128, 64, [3000, 5, 0, 1, 2049, 640], 0, None),
     "d128_ps16": (8, 2, 128, 16, [300, 17, 16, 1000], 0, None),
     "d256_w512": (8, 2, 256, 64, [256, 511, 512, 513, 1536, 900], 512, None),
+    # head_dim 256 at the largest group (G * head_dim = 2048) on 16-token
+    # pages: per-key page lookups in the K copies, the new V row stored apart
+    "d256_g8_ps16": (16, 2, 256, 16, [300, 17, 16, 1000, 0, 65], 0, None),
     "d512_full": (8, 2, 512, 64, [256, 1536, 777], 0, None),
     # G * head_dim = 1536: the merge's 768 dim pairs take 4 per thread (a
     # power of two, so a thread's pairs stay inside one query head)
@@ -70,7 +73,7 @@ LONG_SPLIT_HINT = 1_000_000
 
 
 @pytest.mark.parametrize("hint", [100_000, LONG_SPLIT_HINT])
-@pytest.mark.parametrize("name", [n for n in CASES if CASES[n][2] <= 128])
+@pytest.mark.parametrize("name", [n for n in CASES if CASES[n][2] <= 256])
 def test_decode_long_splits_match_oracle(name, hint):
     n_q, n_kv, D, ps, lengths, window, scale = CASES[name]
     case = make_decode_case(n_q, n_kv, D, ps, lengths, max_slots=len(lengths) + 2,
@@ -94,7 +97,7 @@ def test_decode_long_splits_match_oracle(name, hint):
 
 
 @pytest.mark.parametrize("name", ["tiny", "d128_g4_edges", "d128_ps16", "d256_w512",
-                                  "d512_full"])
+                                  "d256_g8_ps16", "d512_full"])
 def test_decode_fused_append_equals_append_then_decode(name):
     n_q, n_kv, D, ps, lengths, window, scale = CASES[name]
     case = make_decode_case(n_q, n_kv, D, ps, lengths, max_slots=len(lengths) + 2,
