@@ -307,6 +307,7 @@ pkv_status attn_decode_impl(const char* fn, const void* q, int32_t n_q_heads,
   a.scale_log2 = scale * pkv::kLog2eHost;
   a.window = window;
   a.split_tokens = plan.split_tokens;
+  a.head_tokens = plan.head_tokens;
   a.max_splits = plan.max_splits;
   a.waves = plan.waves;
   a.part_o = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;

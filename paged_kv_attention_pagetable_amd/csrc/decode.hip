@@ -99,8 +99,8 @@ __device__ __forceinline__ RowRange row_range(const DecodeArgs& a, int b, int s,
   r.lo = a.window > 0 ? max(0, r.L - a.window) : 0;
   const int base = r.lo & ~31;
   const int span = r.L - base;
-  r.n_valid = min(a.max_splits, (span + a.split_tokens - 1) / a.split_tokens);
   if (a.window > 0) {
+    r.n_valid = min(a.max_splits, (span + a.split_tokens - 1) / a.split_tokens);
     // Sliding window: split 0 takes the range's remainder (span - (n_valid -
     // 1) full splits, rounded up to whole 32-key chunks; beyond max_splits
     // splits it absorbs the excess), splits 1 .. full split_tokens after it.
@@ -112,8 +112,13 @@ __device__ __forceinline__ RowRange row_range(const DecodeArgs& a, int b, int s,
     r.start = s == 0 ? base : base + first + (s - 1) * a.split_tokens;
     r.end = min(r.L, s == 0 ? base + first : r.start + a.split_tokens);
   } else {
-    r.start = base + s * a.split_tokens;
-    r.end = (s == a.max_splits - 1) ? r.L : min(r.L, r.start + a.split_tokens);
+    // Full causal: split 0 takes the first head_tokens keys, splits 1 ..
+    // split_tokens each after it; the last split of the grid also takes any
+    // keys beyond max_splits splits (a length above the plan's hint).
+    const int hs = a.head_tokens;
+    r.n_valid = min(a.max_splits, span <= hs ? 1 : (span - hs + 2 * a.split_tokens - 1) / a.split_tokens);
+    r.start = s == 0 ? base : base + hs + (s - 1) * a.split_tokens;
+    r.end = (s == a.max_splits - 1) ? r.L : min(r.L, r.start + (s == 0 ? hs : a.split_tokens));
   }
   return r;
 }
@@ -887,8 +892,25 @@ DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_h
     split = 32 * 8;
   }
   p.split_tokens = (int)split;
+  p.head_tokens = (int)split;
   p.max_splits = (int)((range + split - 1) / split);
   p.waves = waves;
+  // A short split 0 on large full-causal grids: split 0 of every row is the
+  // last layer of the grid to be dispatched, and the call ends as those
+  // workgroups drain.  A quarter-length split 0 shortens that drain for one
+  // more workgroup per row: Llama shape (4096 workgroups of 512 keys)
+  // 103.0 -> 101.2 us; a 64- or 256-key split 0 measured 104.3 and 102.1.
+  // Below about 2048 workgroups (under three rounds of the resident slots)
+  // the extra workgroups cost more than the drain saves (one GPU's share of
+  // the Llama shape under 8-way tensor parallelism, 512 workgroups: +0.6 us).
+  if (window <= 0 && split >= 512 && pairs * p.max_splits >= 2048) {
+    const int hs = (int)(split / 4);
+    const int n = range <= hs ? 1 : (int)((range - hs + 2 * split - 1) / split);
+    if (n * G <= kMaxMergeUnits) {
+      p.head_tokens = hs;
+      p.max_splits = n;
+    }
+  }
   // (One 8-wave workgroup per pair without a split was measured slower than
   // split + merge even for 8 rows: 64 CUs stream ~16 GB/s each with
   // sequential chunks.)

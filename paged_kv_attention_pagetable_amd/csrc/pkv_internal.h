@@ -70,6 +70,7 @@ struct DecodeArgs {
   float scale_log2;      // softmax scale * log2(e)
   int window;
   int split_tokens;      // keys per split (multiple of 128)
+  int head_tokens;       // keys of split 0 on full-causal rows (<= split_tokens)
   int max_splits;        // grid extent; 1 = no workspace, write out directly
   int waves;             // wave64s per workgroup of the split kernel (4 or 8)
   float* part_o;         // [B][n_kv][max_splits][G][D]
@@ -170,6 +171,7 @@ hipError_t launch_rope_table(float* c, float* s, int max_pos, int head_dim, doub
 // Split-K plan for decode (host): keys per split and grid extent.
 struct DecodePlan {
   int split_tokens;
+  int head_tokens;
   int max_splits;
   int waves;
   size_t ws_bytes;

@@ -37,6 +37,12 @@ CASES = {
     "long_among_short": (32, 8, 128, 64, [4000] + [3, 40, 0, 65, 1, 33, 0] * 4, 0, None),
     # many short rows (80 rows, one split each)
     "many_short": (8, 2, 64, 16, [int(x) for x in np.arange(1, 81) * 7 % 97], 0, None),
+    # 64 rows x 8 kv heads up to 2100 keys: a grid of 2560 512-key splits,
+    # which gets the 128-key split 0; lengths on and around the split edges
+    # (128, 640, 1152, 1664) among seeded ones, idle rows included
+    "head_split": (16, 8, 64, 64, [0, 1, 127, 128, 129, 639, 640, 641, 1151, 1152, 1153, 1663,
+                                   1664, 1665, 2100, 0]
+                   + [int(x) for x in np.arange(1, 49) * 1237 % 2099 + 1], 0, None),
 }
 
 
@@ -97,7 +103,7 @@ def test_decode_long_splits_match_oracle(name, hint):
 
 
 @pytest.mark.parametrize("name", ["tiny", "d128_g4_edges", "d128_ps16", "d256_w512",
-                                  "d256_g8_ps16", "d512_full"])
+                                  "d256_g8_ps16", "d512_full", "head_split"])
 def test_decode_fused_append_equals_append_then_decode(name):
     n_q, n_kv, D, ps, lengths, window, scale = CASES[name]
     case = make_decode_case(n_q, n_kv, D, ps, lengths, max_slots=len(lengths) + 2,
