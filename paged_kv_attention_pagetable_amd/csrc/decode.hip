@@ -139,9 +139,17 @@ __device__ __forceinline__ RowRange row_range(const DecodeArgs& a, int b, int s,
 //   - V (page size >= 32): that chunk loads its whole 32-key group of V
 //     unmasked (the lanes past the last key address the same page), takes
 //     the new key in, and writes the group's 64-byte rows back whole
-//     (NewTok::store_v_rows) before masking the operands.  One 2-byte store
-//     per dim, as a plain append does, is a partial write that the memory
-//     must read, merge and write back: measured 5 us of the Llama call.
+//     (NewTok::store_v_rows) before masking the operands.  In the d-major V
+//     layout the new token touches one row segment per dim: 128 write
+//     bursts per (row, kv head) at head_dim 128, where its K row is two
+//     lines.  Entering HBM while the grid saturates it with reads, these
+//     cost about 4 us of the Llama call, in any form (whole rows, 2-byte
+//     stores, write-through; no extra reads by the counters).  On large
+//     grids (v_late) the owner skips the write and split 0 -- the last
+//     layer of the grid, which runs in its drain -- stores the 2-byte values
+//     at its end instead (NewTok::store_late; Llama shape 100.8 -> 99.5 us).
+//     It fetches the page id and its values when it starts.  On small grids
+//     that store sat on the call's last round trips (Qwen3 +0.6 us).
 //   - K (and V for smaller pages): written after the split's result
 //     (NewTok::store), where no later wait of the workgroup depends on them.
 //     (Written first, the stores sat in front of every chunk load in the
@@ -160,23 +168,34 @@ __device__ __forceinline__ int newtok_v_index(int d) {
   return d - rem + (rem % 16) * (DW / 16) + rem / 16;
 }
 
-template <int D>
+// VL: split 0 writes the new V at its end (the plan's v_late; key-split
+// kernel, page size >= 32); the owner then leaves it out of the pool.
+template <int D, bool VL = false>
 struct NewTok {
   static constexpr int kNV = (D + 255) / 256;  // v values per thread (>= 256 threads)
-  bool on = false;  // this workgroup appends (uniform)
-  int page = -1;    // physical page of key L-1, -1 if unmapped (then nothing is written)
+  bool on = false;    // this workgroup appends (uniform)
+  bool late = false;  // this workgroup (split 0, v_late) writes the new V at its end
+  int page = -1;      // physical page of key L-1, -1 if unmapped (then nothing is written)
+  int late_page = -1;
   u32x4 k{0, 0, 0, 0};
   bf16_t v[kNV] = {};
 
-  __device__ __forceinline__ void load(const DecodeArgs& a, const RowRange& r, int b, int hk) {
-    on = a.k_new && r.end == r.L && ((r.L_in - 1) >> a.g.log2ps) < a.pt.pps;
-    if (!on) return;
+  __device__ __forceinline__ void load(const DecodeArgs& a, const RowRange& r, int b, int hk, int s,
+                                       const int32_t* table) {
+    const bool fits = a.k_new && ((r.L_in - 1) >> a.g.log2ps) < a.pt.pps;
+    on = fits && r.end == r.L;
+    late = VL && fits && s == 0 && a.g.page_size >= 32;
+    if (!on && !late) return;
     const size_t src = ((size_t)b * a.g.n_kv + hk) * D;
-    if ((int)threadIdx.x < D / 8) k = load16(a.k_new + src + 8 * threadIdx.x);
+    if (on && (int)threadIdx.x < D / 8) k = load16(a.k_new + src + 8 * threadIdx.x);
 #pragma unroll
     for (int i = 0; i < kNV; ++i) {
       const int d = threadIdx.x + 256 * i;
       if (d < D) v[i] = a.v_new[src + d];
+    }
+    if (late) {
+      const int pg = table[(size_t)r.slot * a.pt.pps + ((r.L - 1) >> a.g.log2ps)];
+      late_page = (pg >= 1 && pg < a.g.n_pages) ? pg : -1;
     }
   }
   // During the first page staging (a barrier follows); DW = the dims of a
@@ -244,6 +263,20 @@ struct NewTok {
     if (ps >= 32) return;  // V went out whole with its chunk (store_v_rows)
     for (int d = threadIdx.x; d < D; d += blockDim.x)
       a.vpool_w[dst + v_elem_offset(d, row, D, a.g.log2ps)] = L.v[newtok_v_index<DW>(d)];
+  }
+  // v_late, split 0 at its end: the new V, one 2-byte store per dim.
+  __device__ __forceinline__ void store_late(const DecodeArgs& a, const RowRange& r, int hk) const {
+    if (!VL || !late) return;
+    const int pg = __builtin_amdgcn_readfirstlane(late_page);
+    if (pg < 0) return;
+    const int ps = a.g.page_size;
+    const size_t dst = (size_t)pg * a.g.n_kv * ps * D + (size_t)hk * ps * D;
+    const int row = (r.L - 1) & (ps - 1);
+#pragma unroll
+    for (int i = 0; i < kNV; ++i) {
+      const int d = threadIdx.x + 256 * i;
+      if (d < D) a.vpool_w[dst + v_elem_offset(d, row, D, a.g.log2ps)] = v[i];
+    }
   }
   // Page size >= 32, in the chunk holding the new key, after patch(): each
   // lane's 16 bytes of V (rows d0 + 16*dt + lane%16, the 8 keys of its
@@ -436,7 +469,7 @@ __device__ __forceinline__ void idle_output(const DecodeArgs& a, int b, int hk, 
 // ---------------------------------------------------------------------------
 // head_dim <= 128: key split across the NW waves of the workgroup (4, or 8
 // on short splits, see plan_decode); K rows through the waves' LDS stages.
-template <int D, int NW>
+template <int D, int NW, bool VL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void decode_keysplit_kernel(const int32_t* slots, const int32_t* seq_lens, const int32_t* table,
                             int max_splits, DecodeArgs a) {
@@ -461,8 +494,8 @@ void decode_keysplit_kernel(const int32_t* slots, const int32_t* seq_lens, const
     return;
   }
   if (s >= r.n_valid) return;  // past the row's last key: not counted by the merge
-  NewTok<D> nt;
-  nt.load(a, r, b, hk);
+  NewTok<D, VL> nt;
+  nt.load(a, r, b, hk, s, table);
 
   const int ps = a.g.page_size, log2ps = a.g.log2ps;
   const int32_t* trow = table + (size_t)r.slot * a.pt.pps;
@@ -544,7 +577,7 @@ void decode_keysplit_kernel(const int32_t* slots, const int32_t* seq_lens, const
       __atomic_signal_fence(__ATOMIC_SEQ_CST);  // (and the stage reads stay after it)
       if (app) {
         nt.template patch<D>(r, t0, 0, kst, kst_swz<D>, s_new, vop);
-        if (vrows) nt.template store_v_rows<D>(a.vpool_w + (vp - a.vpool), lgv, vop);
+        if (vrows && !VL) nt.template store_v_rows<D>(a.vpool_w + (vp - a.vpool), lgv, vop);
       }
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt)
@@ -635,6 +668,7 @@ void decode_keysplit_kernel(const int32_t* slots, const int32_t* seq_lens, const
   auto Lof = [&](int g) { return s_red[NW * 16 + 16 + g]; };
   finish<D>(a, r, b, hk, s, o_val, Mof, Lof);
   nt.template store<D>(a, r, hk, s_new);
+  nt.store_late(a, r, hk);
 }
 
 // ---------------------------------------------------------------------------
@@ -673,7 +707,7 @@ void decode_dimsplit_kernel(const int32_t* slots, const int32_t* seq_lens, const
   }
   if (s >= r.n_valid) return;  // past the row's last key: not counted by the merge
   NewTok<D> nt;
-  nt.load(a, r, b, hk);
+  nt.load(a, r, b, hk, s, table);
 
   const int dw0 = w * DW;
   u32x4 qreg[DW / 32];  // loaded after the first page staging (see the key-split kernel)
@@ -840,11 +874,15 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.g.n_kv, a.B, a.max_splits);
   if constexpr (D <= 128) {
     if (a.waves == 8)
-      hipLaunchKernelGGL((decode_keysplit_kernel<D, 8>), grid, dim3(8 * 64),
+      hipLaunchKernelGGL((decode_keysplit_kernel<D, 8, false>), grid, dim3(8 * 64),
                          keysplit_lds_bytes<D>(8, a.G), st, a.slots, a.seq_lens, a.pt.table,
                          a.max_splits, a);
+    else if (a.v_late)
+      hipLaunchKernelGGL((decode_keysplit_kernel<D, kDecodeWaves, true>), grid, dim3(kThreads),
+                         keysplit_lds_bytes<D>(kDecodeWaves, a.G), st, a.slots, a.seq_lens,
+                         a.pt.table, a.max_splits, a);
     else
-      hipLaunchKernelGGL((decode_keysplit_kernel<D, kDecodeWaves>), grid, dim3(kThreads),
+      hipLaunchKernelGGL((decode_keysplit_kernel<D, kDecodeWaves, false>), grid, dim3(kThreads),
                          keysplit_lds_bytes<D>(kDecodeWaves, a.G), st, a.slots, a.seq_lens,
                          a.pt.table, a.max_splits, a);
   } else
@@ -893,6 +931,7 @@ DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_h
   }
   p.split_tokens = (int)split;
   p.head_tokens = (int)split;
+  p.v_late = 0;
   p.max_splits = (int)((range + split - 1) / split);
   p.waves = waves;
   // A short split 0 on large full-causal grids: split 0 of every row is the
@@ -909,6 +948,7 @@ DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_h
     if (n * G <= kMaxMergeUnits) {
       p.head_tokens = hs;
       p.max_splits = n;
+      p.v_late = head_dim <= 128;  // (the key-split kernel's fused append)
     }
   }
   // (One 8-wave workgroup per pair without a split was measured slower than

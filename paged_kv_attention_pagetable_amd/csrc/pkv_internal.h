@@ -79,6 +79,9 @@ struct DecodeArgs {
                            // arrivals_end[-1 - (b*n_kv+hk)] (the workspace's last bytes)
   bf16_t* out;           // [B][n_q][D]
   float* lse;            // [B][n_q] or null
+  // (host side, last so that the fields above keep their offsets) launch the
+  // key-split instance whose split 0 writes the fused append's new V at its end
+  int v_late;
 };
 
 // The prologue kernel handles k (normalise, rotate, append) and v (append);
@@ -172,6 +175,7 @@ hipError_t launch_rope_table(float* c, float* s, int max_pos, int head_dim, doub
 struct DecodePlan {
   int split_tokens;
   int head_tokens;
+  int v_late;
   int max_splits;
   int waves;
   size_t ws_bytes;
