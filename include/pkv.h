@@ -151,6 +151,10 @@ pkv_status pkv_append(const void* k_new, const void* v_new, const int32_t* slot,
  * create_causal_blockmask; [moe-qwen3 compare] flex_gemma4_moe.py,
  * _decode_block_mask and _create_sliding_causal_blockmask).  GQA: query head
  * h reads kv head h / (n_q_heads / n_kv_heads).
+ * Numerics: scores, softmax sums and P.V accumulate in fp32 (the softmax
+ * weights enter the P.V product as bf16).  A row split across workgroups
+ * hands each split's normalised output to the merging one as bf16, with its
+ * maximum and sum in fp32; the merge runs in fp32.
  *   q        : device bf16 [B][n_q_heads][head_dim]
  *   slots    : device int32 [B]; seq_lens: device int32 [B]
  *              rows with slot 0 or seq_len 0 are idle: out = 0, lse = -inf,
@@ -204,7 +208,7 @@ pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slot
  * kernels as pkv_attn_decode (its results are bitwise those of
  * pkv_attn_decode for the same inputs); the caller still passes every input
  * and output.  The call allocates nothing and calls no allocating routine.
- * - The buffer is PKV_DECODE_SCRATCH_BYTES (32 MiB) per device, held by each
+ * - The buffer is PKV_DECODE_SCRATCH_BYTES (16 MiB) per device, held by each
  *   device the library runs on until the process ends.  A call whose split
  *   plan needs more (pkv_decode_workspace_size(...) above the limit) returns
  *   PKV_ERR_WORKSPACE and enqueues nothing.
@@ -216,7 +220,7 @@ pkv_status pkv_attn_decode(const void* q, int32_t n_q_heads, const int32_t* slot
  * - The first call on a device looks the buffer's address up
  *   (hipGetSymbolAddress; PKV_ERR_LAUNCH if that fails).
  */
-#define PKV_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+#define PKV_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
 pkv_status pkv_attn_decode_noalloc(const void* q, int32_t n_q_heads, const int32_t* slots,
                                    const int32_t* seq_lens, int32_t B,
                                    int32_t max_seq_len_hint, pkv_page_table pt,

@@ -153,7 +153,7 @@ def attn_decode(q, slots, seq_lens, table, k_pool, v_pool, scale=None, window=0,
     return out
 
 
-DECODE_SCRATCH_BYTES = 32 << 20   # the library's static scratch per device
+DECODE_SCRATCH_BYTES = 16 << 20   # the library's static scratch per device
 
 
 def attn_decode_noalloc(q, slots, seq_lens, table, k_pool, v_pool, out, scale=None, window=0,

@@ -73,7 +73,7 @@ struct DecodeArgs {
   int head_tokens;       // keys of split 0 on full-causal rows (<= split_tokens)
   int max_splits;        // grid extent; 1 = no workspace, write out directly
   int waves;             // wave64s per workgroup of the split kernel (4 or 8)
-  float* part_o;         // [B][n_kv][max_splits][G][D]
+  uint32_t* part_o;      // [B][n_kv][max_splits][G][D/2] bf16 pairs of the split's o / l
   float* part_ml;        // [B][n_kv][max_splits][G][2]  (running max in log2 units, sum)
   uint32_t* arrivals_end;  // one past the split arrival counters: pair b*n_kv+hk at
                            // arrivals_end[-1 - (b*n_kv+hk)] (the workspace's last bytes)
@@ -179,7 +179,7 @@ struct DecodePlan {
   int max_splits;
   int waves;
   size_t ws_bytes;
-  size_t part_o_floats;  // partial outputs first, then the (max, sum) pairs
+  size_t part_o_words;   // partial outputs first (bf16 pairs), then the fp32 (max, sum) pairs
 };
 DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_hint,
                        int window);
@@ -194,7 +194,7 @@ inline size_t decode_counter_region(size_t ws) { return (ws / 16) & ~(size_t)15;
 // Static split-K scratch of pkv_attn_decode_noalloc: one buffer of this many
 // bytes per device, inside the library's code object.  decode_scratch gives
 // the current device's copy (its address is looked up once per device).
-constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
 hipError_t decode_scratch(void** ptr);
 
 // Query tokens per prefill workgroup for a GQA ratio.

@@ -72,7 +72,7 @@ def test_noalloc_matches_workspace_call_twice_second_smaller():
 
 def test_noalloc_rejects_a_plan_beyond_the_scratch():
     """32 rows of G 8, head_dim 256 over 16384 keys: the split partials need
-    more than the 32 MiB scratch; the call fails on the host and enqueues
+    more than the 16 MiB scratch; the call fails on the host and enqueues
     nothing (out keeps its fill)."""
     need = pkv.decode_workspace_size(32, 8, 1, 256, 16384, 0)
     assert need > pkv.DECODE_SCRATCH_BYTES
