@@ -427,14 +427,17 @@ def _pmc_record(part):
 
 def pmc_traffic(part, instance=None):
     """HBM bytes per call from a committed rocprofv3 PMC summary, if current:
-    of the part's counted kernels, or of one kernel ``instance`` of it."""
+    of the part's counted kernels, or of the kernel whose name starts with
+    ``instance`` (a template name and its first arguments, e.g.
+    ``decode_dimsplit_kernel<512``; one instance ran per such prefix)."""
     rec = _pmc_record(part)
     if rec is None:
         return None
     if instance is None:
         return rec.get("hbm_bytes_per_call")
-    k = rec.get("kernels", {}).get(instance)
-    return None if k is None else k["fetch_bytes"] + k["write_bytes"]
+    ks = [k for name, k in rec.get("kernels", {}).items()
+          if name.startswith(instance) and name[len(instance):len(instance) + 1] in (">", ",")]
+    return ks[0]["fetch_bytes"] + ks[0]["write_bytes"] if len(ks) == 1 else None
 
 
 # ----------------------------------------------------------------------------
@@ -795,7 +798,7 @@ def decode_record(name, args, headline=False):
                 achieved=round(b / (ms * 1e-3) / 1e9, 1),
                 frac=round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 traffic=None if args.contiguous_pages else pmc_traffic(
-                    f"decode_{name}", f"decode_dimsplit_kernel<{D}>"),
+                    f"decode_{name}", f"decode_dimsplit_kernel<{D}"),
                 window=max(ly["window"] for ly in lys))
             del g
     if args.attn_only:

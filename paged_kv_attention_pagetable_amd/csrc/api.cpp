@@ -309,6 +309,7 @@ pkv_status attn_decode_impl(const char* fn, const void* q, int32_t n_q_heads,
   a.split_tokens = plan.split_tokens;
   a.head_tokens = plan.head_tokens;
   a.v_late = plan.v_late;
+  a.early_merge = plan.early_merge;
   a.max_splits = plan.max_splits;
   a.waves = plan.waves;
   a.part_o = plan.ws_bytes ? static_cast<uint32_t*>(workspace) : nullptr;

@@ -79,9 +79,12 @@ struct DecodeArgs {
                            // arrivals_end[-1 - (b*n_kv+hk)] (the workspace's last bytes)
   bf16_t* out;           // [B][n_q][D]
   float* lse;            // [B][n_q] or null
-  // (host side, last so that the fields above keep their offsets) launch the
-  // key-split instance whose split 0 writes the fused append's new V at its end
+  // (host side, last so that the fields above keep their offsets) kernel
+  // instance selection: v_late, the key-split instance whose split 0 writes
+  // the fused append's new V at its end (and merges early); early_merge, the
+  // dim-split instance whose split 0 merges early
   int v_late;
+  int early_merge;
 };
 
 // The prologue kernel handles k (normalise, rotate, append) and v (append);
@@ -176,6 +179,7 @@ struct DecodePlan {
   int split_tokens;
   int head_tokens;
   int v_late;
+  int early_merge;
   int max_splits;
   int waves;
   size_t ws_bytes;
