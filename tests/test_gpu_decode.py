@@ -262,6 +262,39 @@ def test_decode_bitwise_deterministic_and_page_permutation_invariant():
     assert torch.equal(o4.view(torch.int16), o5.view(torch.int16)) and torch.equal(l4, l5)
 
 
+@pytest.mark.parametrize("shape", ["head_split", "d512_rounds"])
+def test_decode_split0_early_merge_bitwise(shape):
+    """On grids of several rounds split 0 merges at once, with its own values,
+    when the row's other splits are already in, else publishes its partial
+    like any split: which path runs depends on timing.  Repeated calls (with
+    and without the fused append) must agree bit for bit, and with the
+    oracle.  head_split: 2560 key-split workgroups; d512_rounds: 48 rows x 2
+    kv heads at head_dim 512, 1152 dim-split workgroups."""
+    if shape == "head_split":
+        n_q, n_kv, D, ps, lengths, window, scale = CASES["head_split"]
+    else:
+        rng = np.random.default_rng(31)
+        n_q, n_kv, D, ps, window, scale = 8, 2, 512, 64, 0, None
+        lengths = [int(x) for x in rng.integers(256, 1537, size=48)]
+    case = make_decode_case(n_q, n_kv, D, ps, lengths, max_slots=len(lengths) + 2, seed=1700 + D,
+                            window=window, scale=scale, spare_pages=2)
+    kp, vp, table = gpu_decode_setup(case)
+    outs = [run_gpu_decode(case, kp, vp, table) for _ in range(4)]
+    for o, l in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(l, outs[0][1])
+    okp, ovp = oracle_decode_pools(case)
+    ref, _ = oracle.attn_decode(case.q, okp, ovp, case.table, case.slots, case.seq_lens,
+                                case.scale, case.window)
+    assert_attn_close(host_f64(outs[0][0]), ref, shape)
+    for _ in range(2):
+        kp2, vp2, table2 = gpu_decode_setup(case, with_new_token=False)
+        o2, l2 = run_gpu_decode(case, kp2, vp2, table2, fused_append=True)
+        assert torch.equal(o2.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(l2, outs[0][1])
+        assert np.array_equal(host_bits(kp2), okp) and np.array_equal(host_bits(vp2), ovp)
+
+
 def test_decode_window_at_least_length_equals_full_bitwise():
     case = make_decode_case(8, 2, 128, 64, [300, 77, 512], max_slots=5, seed=9)
     kp, vp, table = gpu_decode_setup(case)
