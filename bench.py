@@ -601,6 +601,59 @@ def summarize_mfma(db_path, out_path, command=""):
     print(json.dumps(rec))
 
 
+SQ_INSTANCES = {
+    # summary key: SQL name pattern of the kernel instance
+    "prefill_attention": "%prefill_kernel<%, 0>%",
+    "prefill_attention_fused_q": "%prefill_kernel<%, 2>%",
+    "decode_llama": "%decode_keysplit_kernel<128, 4, true>%",
+}
+
+
+def summarize_sq(db_paths, out_path, command=""):
+    """Shader-sequencer counters of the prefill instances (and, for contrast,
+    the Llama decode kernel) from one or more `rocprofv3 --pmc` runs, each
+    counter's mean per dispatch.  Derived: the share of wave-cycles spent
+    waiting (SQ_WAIT_ANY), waiting to issue an LDS instruction
+    (SQ_WAIT_INST_LDS) and issuing VALU / LDS / vector-memory instructions
+    (SQ_ACTIVE_INST_*), all over SQ_WAVE_CYCLES; LDS bank-conflict cycles over
+    LDS-active cycles; MFMA busy over all SIMD cycles."""
+    import sqlite3
+    recs = {}
+    for name, key in SQ_INSTANCES.items():
+        vals, durs = {}, []
+        for path in db_paths.split(","):
+            db = sqlite3.connect(path)
+            names = [r[0] for r in db.execute(
+                "select distinct counter_name from pmc_events where name like ?", (key,))]
+            for c in names:
+                rows = db.execute("select dispatch_id, sum(counter_value) from pmc_events where name "
+                                  "like ? and counter_name = ? group by dispatch_id", (key, c)).fetchall()
+                vals[c] = float(np.mean([r[1] for r in rows]))
+            durs += [r[0] for r in db.execute("select duration from kernels where name like ?", (key,))]
+        if not vals:
+            continue
+        rec = dict(counters=vals, kernel_ns_under_counters=float(np.mean(durs)) if durs else None)
+        wc = vals.get("SQ_WAVE_CYCLES")
+        if wc:
+            for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_ANY",
+                      "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM",
+                      "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_MISC"):
+                if c in vals:
+                    rec[c.lower()[3:] + "_over_wave_cycles"] = round(vals[c] / wc, 4)
+        if vals.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in vals:
+            rec["lds_bank_conflict_over_lds_active"] = round(
+                vals["SQ_LDS_BANK_CONFLICT"] / vals["SQ_LDS_IDX_ACTIVE"], 4)
+        gui, busy = vals.get("GRBM_GUI_ACTIVE"), vals.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        if gui and busy:
+            rec["mfma_busy_fraction"] = round(busy / (gui / N_XCD * N_CU * 4), 4)
+        recs[name] = rec
+    out = dict(source_sha=dict(prefill=source_sha(PREFILL_SRC), decode=source_sha(DECODE_SRC)),
+               instances=recs, command=command)
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps({k: {kk: vv for kk, vv in v.items() if kk != "counters"} for k, v in recs.items()}))
+
+
 # ----------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample)
 # ----------------------------------------------------------------------------
@@ -923,6 +976,8 @@ def main():
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("DB", "OUT"),
                     help="write the prefill kernel's matrix-core counters from one rocprofv3 "
                          "--pmc run and exit")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("DBS", "OUT"),
+                    help="write the SQ counter summary of comma-separated --pmc databases and exit")
     ap.add_argument("--command", default="", help="command line recorded in summaries")
     args = ap.parse_args()
     if args.summarize_trace:
@@ -930,6 +985,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma, command=args.command)
+        return
+    if args.summarize_sq:
+        summarize_sq(*args.summarize_sq, command=args.command)
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, command=args.command,
