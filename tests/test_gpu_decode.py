@@ -43,6 +43,11 @@ CASES = {
     "head_split": (16, 8, 64, 64, [0, 1, 127, 128, 129, 639, 640, 641, 1151, 1152, 1153, 1663,
                                    1664, 1665, 2100, 0]
                    + [int(x) for x in np.arange(1, 49) * 1237 % 2099 + 1], 0, None),
+    # the same grid on 16-token pages: the large-grid kernel instance, whose
+    # split 0 writes the new V only for pages of 32 keys or more, so here the
+    # owner still writes it
+    "head_split_ps16": (16, 8, 64, 16, [0, 1, 15, 16, 17, 127, 128, 129, 639, 640, 641, 2100]
+                        + [int(x) for x in np.arange(1, 53) * 1237 % 2099 + 1], 0, None),
 }
 
 
@@ -103,7 +108,7 @@ def test_decode_long_splits_match_oracle(name, hint):
 
 
 @pytest.mark.parametrize("name", ["tiny", "d128_g4_edges", "d128_ps16", "d256_w512",
-                                  "d256_g8_ps16", "d512_full", "head_split"])
+                                  "d256_g8_ps16", "d512_full", "head_split", "head_split_ps16"])
 def test_decode_fused_append_equals_append_then_decode(name):
     n_q, n_kv, D, ps, lengths, window, scale = CASES[name]
     case = make_decode_case(n_q, n_kv, D, ps, lengths, max_slots=len(lengths) + 2,
