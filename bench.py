@@ -17,7 +17,11 @@ instance is also the Llama step's, so its counter traffic comes from a run of
 it alone) -- are
 reported under ``extra_decode`` with their own rooflines, and the Qwen3-4B chunked prefill
 (16 prompts U[32, 512], fused q/k RMSNorm + RoPE + append prologue, then MFMA
-prefill attention, 36 layers) under ``prefill``.
+prefill attention, 36 layers) under ``prefill``.  ``extra_prefill`` adds the
+Gemma-4-shaped prefill layers with their prologue (sliding head_dim 256 and
+full head_dim 512) and a Qwen3-shaped launch of prompt chunks on cached
+prefixes mixed with decode rows: per call, a whole layer and the attention
+with the fused q transform, against both rooflines.
 
 Every phase is captured once in a HIP graph (through torch.cuda.CUDAGraph) and
 replayed: inputs are resident in HBM before the timed region, and the timed
@@ -274,6 +278,174 @@ class PrefillWorkload:
                     n_q=c["n_q"], n_kv=c["n_kv"], head_dim=c["head_dim"],
                     page_size=c["page_size"], layers=c["layers"],
                     lengths=f"U[{c['len_lo']},{c['len_hi']}]", prologue="rmsnorm+rope theta 1e6")
+
+
+class _PrefillLayers:
+    """Copies of one prefill layer shape (own pools, q, k, v, out each), for
+    the extra prefill workloads: a whole layer is the prologue + attention
+    call, and the attention alone is the call with only the q transform
+    (keys already appended by an earlier layer call)."""
+
+    N_COPIES = 4   # layer calls per captured graph
+
+    def __init__(self, pkv, rnd, dev, n_q, n_kv, D, ps, n_pages, T, theta, max_pos, eps,
+                 fraction=1.0, k_eq_v=False, prefill_pools=False):
+        import torch
+        self.pkv, self.D, self.eps = pkv, D, eps
+        self.cos, self.sin = pkv.rope_table(max_pos, D, theta, dev, rotary_fraction=fraction)
+        self.copies = []
+        for _ in range(self.N_COPIES):
+            kp, vp = pkv.new_pools(n_pages, n_kv, ps, D, dev, fill=-1)
+            if prefill_pools:   # cached prefixes: random rows on every page
+                kp.copy_(rnd.bf16(tuple(kp.shape)))
+                vp.copy_(rnd.bf16(tuple(vp.shape)))
+            k = rnd.bf16((T, n_kv, D))
+            self.copies.append(dict(
+                kp=kp, vp=vp, q=rnd.bf16((T, n_q, D)), k=k,
+                v=k if k_eq_v else rnd.bf16((T, n_kv, D)), qw=rnd.bf16((D,), 1.0, 0.1),
+                kw=rnd.bf16((D,), 1.0, 0.1),
+                out=torch.empty((T, n_q, D), dtype=torch.bfloat16, device=dev)))
+
+    def run(self, w, with_kv, v_norm, window):
+        for ly in self.copies:
+            pro = dict(q_norm_w=ly["qw"], eps=self.eps, cos=self.cos, sin=self.sin)
+            if with_kv:
+                pro.update(k_norm_w=ly["kw"], k=ly["k"], v=ly["v"], v_norm=v_norm)
+            self.pkv.attn_prefill(ly["q"], w.cu, w.slots, w.table, ly["kp"], ly["vp"],
+                                  scale=1.0 / math.sqrt(self.D), window=window,
+                                  start_pos=w.start, max_seqlen_q_hint=w.hint, prologue=pro,
+                                  out=ly["out"])
+
+
+def _prefill_flops(new, prefix, n_q, D, window):
+    """Attention FLOPs (2 for QK^T and 2 for PV per visible query-key pair) of
+    sequences of ``new`` queries after ``prefix`` cached keys."""
+    tot = 0
+    for L, P in zip(np.asarray(new, dtype=np.int64), np.asarray(prefix, dtype=np.int64)):
+        keys = P + np.arange(1, L + 1)
+        if window > 0:
+            keys = np.minimum(keys, window)
+        tot += int(keys.sum())
+    return 4 * D * n_q * tot
+
+
+def _prefill_bytes(new, prefix, n_q, n_kv, D, ps):
+    """Compulsory bytes of one attention call: q read and out written once,
+    each sequence's K and V rows (prefix and new) read once, its page ids."""
+    new = np.asarray(new, dtype=np.int64)
+    keys = new + np.asarray(prefix, dtype=np.int64)
+    return (int(new.sum()) * n_q * D * 2 * 2 + int(keys.sum()) * n_kv * D * 2 * 2
+            + int(np.ceil(keys / ps).sum()) * 4)
+
+
+class GemmaPrefillWorkload:
+    """Gemma-4-shaped prefill with its prologue: a sliding layer and a
+    full-attention layer (head_dim 256 and 512), see synth's gemma_prefill."""
+
+    def __init__(self, device="cuda"):
+        import torch
+
+        import paged_kv_attention_pagetable_amd as pkv
+        from synth import CONFIGS, config_lengths, prefill_page_table, split_tokens
+        from synth.device import DeviceRandom
+        c = self.c = CONFIGS["gemma_prefill"]
+        self.new, slots = config_lengths("gemma_prefill")
+        self.prefix = np.zeros_like(self.new)
+        ps = c["page_size"]
+        n_pages, table = prefill_page_table(ps, self.new, self.prefix, slots, c["max_slots"],
+                                            3407 + c["index"], -(-c["len_hi"] // ps))
+        self.table = torch.from_numpy(table).to(device)
+        self.slots = torch.from_numpy(slots).to(device)
+        self.cu = torch.from_numpy(split_tokens(self.new)).to(device)
+        self.start = torch.from_numpy(self.prefix).to(device)
+        self.hint = c["len_hi"]
+        T = int(self.new.sum())
+        rnd = DeviceRandom(3407 + 100 * c["index"], device)
+        self.kinds = {
+            c["sliding_dim"]: (_PrefillLayers(pkv, rnd, device, c["n_q"], c["n_kv"],
+                                              c["sliding_dim"], ps, n_pages, T,
+                                              c["sliding_theta"], c["len_hi"] + 1, c["eps"]),
+                               c["window"]),
+            c["full_dim"]: (_PrefillLayers(pkv, rnd, device, c["n_q"], c["n_kv"], c["full_dim"],
+                                           ps, n_pages, T, c["full_theta"], c["len_hi"] + 1,
+                                           c["eps"], fraction=c["full_rotary"], k_eq_v=True),
+                            0),
+        }
+        torch.cuda.synchronize()
+
+    def layer(self, D):
+        lay, window = self.kinds[D]
+        lay.run(self, True, True, window)
+
+    def attn_fused_q(self, D):
+        lay, window = self.kinds[D]
+        lay.run(self, False, True, window)
+
+    def flops(self, D):
+        return _prefill_flops(self.new, self.prefix, self.c["n_q"], D, self.kinds[D][1])
+
+    def attn_bytes(self, D):
+        c = self.c
+        return _prefill_bytes(self.new, self.prefix, c["n_q"], c["n_kv"], D, c["page_size"])
+
+    def describe(self):
+        c = self.c
+        return dict(workload="gemma_prefill", prompts=len(self.new), tokens=int(self.new.sum()),
+                    n_q=c["n_q"], n_kv=c["n_kv"], page_size=c["page_size"],
+                    lengths=f"U[{c['len_lo']},{c['len_hi']}]",
+                    layers="sliding D 256 (window 512, theta 1e4) + full D 512 (theta 1e6, "
+                           "25 % rotary, K = V); v_norm")
+
+
+class ChunkedMixedWorkload:
+    """Qwen3-shaped prompt chunks on cached prefixes and decode rows in one
+    prefill launch with the Qwen3 prologue, see synth's qwen3_chunked_mixed."""
+
+    def __init__(self, device="cuda"):
+        import torch
+
+        import paged_kv_attention_pagetable_amd as pkv
+        from synth import CONFIGS, chunked_mixed_rows, prefill_page_table, split_tokens
+        from synth.device import DeviceRandom
+        c = self.c = CONFIGS["qwen3_chunked_mixed"]
+        self.new, self.prefix, slots = chunked_mixed_rows()
+        ps, D = c["page_size"], c["head_dim"]
+        total = self.new + self.prefix
+        n_pages, table = prefill_page_table(ps, self.new, self.prefix, slots, c["max_slots"],
+                                            3407 + c["index"], -(-int(total.max()) // ps))
+        self.table = torch.from_numpy(table).to(device)
+        self.slots = torch.from_numpy(slots).to(device)
+        self.cu = torch.from_numpy(split_tokens(self.new)).to(device)
+        self.start = torch.from_numpy(self.prefix).to(device)
+        self.hint = c["chunk_hi"]
+        T = int(self.new.sum())
+        rnd = DeviceRandom(3407 + 100 * c["index"], device)
+        self.lay = _PrefillLayers(pkv, rnd, device, c["n_q"], c["n_kv"], D, ps, n_pages, T,
+                                  c["theta"], int(total.max()) + 1, c["eps"], prefill_pools=True)
+        torch.cuda.synchronize()
+
+    def layer(self):
+        self.lay.run(self, True, False, 0)
+
+    def attn_fused_q(self):
+        self.lay.run(self, False, False, 0)
+
+    def flops(self):
+        return _prefill_flops(self.new, self.prefix, self.c["n_q"], self.c["head_dim"], 0)
+
+    def attn_bytes(self):
+        c = self.c
+        return _prefill_bytes(self.new, self.prefix, c["n_q"], c["n_kv"], c["head_dim"],
+                              c["page_size"])
+
+    def describe(self):
+        c = self.c
+        return dict(workload="qwen3_chunked_mixed", chunks=c["n_chunks"],
+                    chunk=f"U[{c['chunk_lo']},{c['chunk_hi']}]",
+                    prefix=f"U[{c['prefix_lo']},{c['prefix_hi']}]", decode_rows=c["n_decode"],
+                    decode_context=f"U[{c['ctx_lo']},{c['ctx_hi']})", tokens=int(self.new.sum()),
+                    n_q=c["n_q"], n_kv=c["n_kv"], head_dim=c["head_dim"],
+                    page_size=c["page_size"], prologue="rmsnorm+rope theta 1e6")
 
 
 # ----------------------------------------------------------------------------
@@ -936,6 +1108,61 @@ def prefill_record(args):
     return rec
 
 
+def _extra_prefill_roofs(fl, ab, ms_layer, ms_attn, kernel):
+    tf = fl / (ms_attn * 1e-3) / 1e12
+    gbs = ab / (ms_attn * 1e-3) / 1e9
+    return dict(
+        us_per_layer=round(ms_layer * 1e3, 3), prologue_us=round((ms_layer - ms_attn) * 1e3, 3),
+        roofline=dict(bound="mfma", achieved=round(tf, 2), peak=MFMA_BF16_PEAK_TFLOPS,
+                      unit="TFLOP/s", frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None,
+                      kernel=kernel, algorithmic_flops_per_call=fl,
+                      us_per_call=round(ms_attn * 1e3, 3)),
+        roofline_hbm=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                          frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None,
+                          algorithmic_bytes_per_call=ab, us_per_call=round(ms_attn * 1e3, 3),
+                          arithmetic_intensity=round(fl / ab, 1)))
+
+
+def extra_prefill_records(args):
+    """The Gemma-4 prefill layers and the chunked prefill + decode launch:
+    per call, a whole layer (prologue + attention) and the attention with the
+    fused q transform alone, each against the MFMA and HBM rooflines."""
+    import torch
+    out = {}
+    log("setting up gemma_prefill")
+    gw = GemmaPrefillWorkload()
+    rec = dict(config=gw.describe(), per_kind={})
+    for D in sorted(gw.kinds):
+        g_l = capture(lambda D=D: gw.layer(D))
+        g_a = capture(lambda D=D: gw.attn_fused_q(D))
+        n = _PrefillLayers.N_COPIES
+        ms_l = time_graph(g_l, args.kernel_reps, 2) / n
+        ms_a = time_graph(g_a, args.kernel_reps, 2) / n
+        rec["per_kind"][f"head_dim_{D}"] = dict(
+            window=gw.kinds[D][1], **_extra_prefill_roofs(
+                gw.flops(D), gw.attn_bytes(D), ms_l, ms_a,
+                f"prefill attention with the fused q transform, head_dim {D}"))
+        del g_l, g_a
+    out["gemma_prefill"] = rec
+    del gw
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log("setting up qwen3_chunked_mixed")
+    mw = ChunkedMixedWorkload()
+    g_l = capture(mw.layer)
+    g_a = capture(mw.attn_fused_q)
+    n = _PrefillLayers.N_COPIES
+    ms_l = time_graph(g_l, args.kernel_reps, 2) / n
+    ms_a = time_graph(g_a, args.kernel_reps, 2) / n
+    out["qwen3_chunked_mixed"] = dict(config=mw.describe(), **_extra_prefill_roofs(
+        mw.flops(), mw.attn_bytes(), ms_l, ms_a,
+        "prefill attention with the fused q transform (prompt chunks and decode rows)"))
+    del g_l, g_a, mw
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -952,6 +1179,8 @@ def main():
     ap.add_argument("--no-extra-decode", action="store_true",
                     help="skip the other decode workloads")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extra-prefill", action="store_true",
+                    help="skip the Gemma-4 prefill layers and the chunked prefill + decode launch")
     ap.add_argument("--attn-only", action="store_true",
                     help="also time decode attention without the fused append")
     ap.add_argument("--contiguous-pages", action="store_true",
@@ -1037,6 +1266,8 @@ def main():
         del src, dst
     if not args.no_prefill:
         result["prefill"] = prefill_record(args)
+        if not args.no_extra_prefill:
+            result["extra_prefill"] = extra_prefill_records(args)
 
     if not args.no_cpu_baseline:
         procs = args.cpu_processes or min(len(os.sched_getaffinity(0)), 16)

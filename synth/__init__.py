@@ -21,6 +21,13 @@ N(0,1) bf16 tensors of the same shapes stand in for them):
 * ``gemma_mixed``   64 rows, lengths U[256, 1536], n_q 8 / n_kv 2, page 64;
                     one sliding layer (D 256, window 512) and one full layer
                     (D 512) per step.
+* ``gemma_prefill`` 16 prompts U[128, 1024], n_q 8 / n_kv 2, page 64, the
+                    Gemma-4 prologue; a sliding layer (D 256, window 512,
+                    theta 1e4) and a full layer (D 512, theta 1e6, 25 %
+                    rotary, K = V).
+* ``qwen3_chunked_mixed`` one launch of 8 prompt chunks U[64, 512] on cached
+                    prefixes U[256, 1024] and 56 decode rows (one token on a
+                    cached U[64, 1024]); Qwen3 heads and prologue.
 
 Seeds are ``3407 + config index`` (3407 is the seed the pages' scripts use).
 """
@@ -36,4 +43,6 @@ from .gen import (  # noqa: F401
     make_prefill_case,
     split_tokens,
     config_lengths,
+    chunked_mixed_rows,
+    prefill_page_table,
 )

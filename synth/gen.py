@@ -32,6 +32,20 @@ CONFIGS = {
     "gemma_mixed": dict(index=4, n_q=8, n_kv=2, page_size=64, B=64, max_slots=65,
                         len_lo=256, len_hi=1536, sliding_dim=256, window=512,
                         full_dim=512, layers=4),
+    # Gemma-4-shaped prefill with its prologue: a sliding layer (head_dim 256,
+    # window 512, theta 1e4, full rotary) and a full-attention layer (head_dim
+    # 512, theta 1e6, 25 % rotary, K = V); v_norm on both.  Prompts up to 1024
+    # tokens, so the window cuts the longer ones.
+    "gemma_prefill": dict(index=5, n_q=8, n_kv=2, page_size=64, n_seqs=16, max_slots=17,
+                          len_lo=128, len_hi=1024, eps=1e-6, sliding_dim=256, window=512,
+                          sliding_theta=1e4, full_dim=512, full_theta=1e6, full_rotary=0.25),
+    # Qwen3-shaped chunked prefill mixed with decode in one launch: 8 prompt
+    # chunks of U[64,512] new tokens on cached prefixes of U[256,1024], and 56
+    # decode rows (one new token on a cached U[64,1024]); the Qwen3 prologue.
+    "qwen3_chunked_mixed": dict(index=6, n_q=32, n_kv=8, head_dim=128, page_size=128,
+                                n_chunks=8, chunk_lo=64, chunk_hi=512, prefix_lo=256,
+                                prefix_hi=1024, n_decode=56, ctx_lo=64, ctx_hi=1024,
+                                max_slots=65, eps=1e-6, theta=1e6),
 }
 
 
@@ -304,7 +318,32 @@ def config_lengths(name: str, salt: int = 0):
     if name == "gemma_mixed":
         L = rng.integers(c["len_lo"], c["len_hi"] + 1, size=c["B"]).astype(np.int32)
         return L, np.arange(1, c["B"] + 1, dtype=np.int32)
-    if name == "qwen3_prefill":
+    if name in ("qwen3_prefill", "gemma_prefill"):
         L = rng.integers(c["len_lo"], c["len_hi"] + 1, size=c["n_seqs"]).astype(np.int32)
         return L, np.arange(1, c["n_seqs"] + 1, dtype=np.int32)
     raise KeyError(name)
+
+
+def chunked_mixed_rows(name: str = "qwen3_chunked_mixed"):
+    """(new tokens, cached prefix, slots) per sequence of the mixed launch:
+    the prompt chunks first, then the decode rows (one new token each)."""
+    c = CONFIGS[name]
+    rng = rng_for(c["index"])
+    n1, n2 = c["n_chunks"], c["n_decode"]
+    new = np.concatenate([rng.integers(c["chunk_lo"], c["chunk_hi"] + 1, size=n1),
+                          np.ones(n2, dtype=np.int64)]).astype(np.int32)
+    prefix = np.concatenate([rng.integers(c["prefix_lo"], c["prefix_hi"] + 1, size=n1),
+                             rng.integers(c["ctx_lo"], c["ctx_hi"], size=n2)]).astype(np.int32)
+    return new, prefix, np.arange(1, n1 + n2 + 1, dtype=np.int32)
+
+
+def prefill_page_table(page_size, lengths, start_pos, slots, max_slots, seed, pages_per_slot,
+                       spare_pages=2):
+    """(n_pages, table) for sequences of ``start_pos + lengths`` keys on a
+    seeded random page permutation (no token data drawn)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    total = np.asarray(lengths, dtype=np.int64) + np.asarray(start_pos, dtype=np.int64)
+    slot_lengths = {int(slots[i]): int(total[i]) for i in range(len(total))
+                    if slots[i] != 0 and total[i] > 0}
+    return _page_assignment(rng, slot_lengths, page_size, pages_per_slot, max_slots,
+                            spare_pages)
