@@ -56,8 +56,12 @@ constexpr int kStagePages = 2048;         // page ids staged in LDS (>= pages_pe
 // Waves per workgroup and 16-column MFMA tiles per wave: 4 waves of up to
 // 256 registers, two waves per SIMD (two workgroups per CU).  (8 waves of
 // one tile at 128 registers, four per SIMD, measured no faster and spills.)
+// head_dim 256: its double-buffered 64 KB tiles leave room for one
+// workgroup per CU, so 8 waves of one tile (198-204 registers, two waves per
+// SIMD) -- twice the occupancy of 4, and items of twice the tokens, so half
+// the key re-reads: the Gemma-4 sliding layer 80.9 -> 57.5 us.
 template <int D>
-constexpr int prefill_waves() { return 4; }
+constexpr int prefill_waves() { return D == 256 ? 8 : 4; }
 template <int D>
 constexpr int prefill_threads() { return 64 * prefill_waves<D>(); }
 template <int D>
