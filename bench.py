@@ -670,6 +670,10 @@ PMC_PARTS = {
     # prefill attention with the fused q norm + RoPE: with 4 query heads per
     # kv head, the instance whose rotary rows are staged in LDS (q mode 2)
     "prefill_fused_q_qwen3_prefill": (("prefill_kernel<", ", 2>"), PREFILL_SRC),
+    # the Gemma-4 prefill layers (extra_prefill): head_dim 256 and 512 with
+    # the q transform loading its rotary rows (q mode 1); no other part runs them
+    "prefill_gemma_prefill_d256": (("prefill_kernel<256, ", ", 1>"), PREFILL_SRC),
+    "prefill_gemma_prefill_d512": (("prefill_kernel<512, ", ", 1>"), PREFILL_SRC),
 }
 # Parts whose kernel instance another workload runs too: summarized only from
 # a counter run of that workload alone (``--pmc-parts``; bench.py
@@ -1108,17 +1112,18 @@ def prefill_record(args):
     return rec
 
 
-def _extra_prefill_roofs(fl, ab, ms_layer, ms_attn, kernel):
+def _extra_prefill_roofs(fl, ab, ms_layer, ms_attn, kernel, part=None):
     tf = fl / (ms_attn * 1e-3) / 1e12
     gbs = ab / (ms_attn * 1e-3) / 1e9
+    traffic = pmc_traffic(part) if part else None
     return dict(
         us_per_layer=round(ms_layer * 1e3, 3), prologue_us=round((ms_layer - ms_attn) * 1e3, 3),
         roofline=dict(bound="mfma", achieved=round(tf, 2), peak=MFMA_BF16_PEAK_TFLOPS,
-                      unit="TFLOP/s", frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None,
+                      unit="TFLOP/s", frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4), traffic=traffic,
                       kernel=kernel, algorithmic_flops_per_call=fl,
                       us_per_call=round(ms_attn * 1e3, 3)),
         roofline_hbm=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                          frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None,
+                          frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic,
                           algorithmic_bytes_per_call=ab, us_per_call=round(ms_attn * 1e3, 3),
                           arithmetic_intensity=round(fl / ab, 1)))
 
@@ -1141,7 +1146,8 @@ def extra_prefill_records(args):
         rec["per_kind"][f"head_dim_{D}"] = dict(
             window=gw.kinds[D][1], **_extra_prefill_roofs(
                 gw.flops(D), gw.attn_bytes(D), ms_l, ms_a,
-                f"prefill attention with the fused q transform, head_dim {D}"))
+                f"prefill attention with the fused q transform, head_dim {D}",
+                part=f"prefill_gemma_prefill_d{D}"))
         del g_l, g_a
     out["gemma_prefill"] = rec
     del gw
