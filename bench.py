@@ -670,18 +670,23 @@ PMC_PARTS = {
     # prefill attention with the fused q norm + RoPE: with 4 query heads per
     # kv head, the instance whose rotary rows are staged in LDS (q mode 2)
     "prefill_fused_q_qwen3_prefill": (("prefill_kernel<", ", 2>"), PREFILL_SRC),
-    # the Gemma-4 prefill layers (extra_prefill): head_dim 256 and 512 with
-    # the q transform loading its rotary rows (q mode 1); no other part runs them
-    "prefill_gemma_prefill_d256": (("prefill_kernel<256, ", ", 1>"), PREFILL_SRC),
-    "prefill_gemma_prefill_d512": (("prefill_kernel<512, ", ", 1>"), PREFILL_SRC),
 }
-# Parts whose kernel instance another workload runs too: summarized only from
-# a counter run of that workload alone (``--pmc-parts``; bench.py
-# --workload <name> --no-extra-decode --no-prefill).
+# Parts summarized only from counter runs named for them (``--pmc-parts``):
+# the tensor-parallel share, whose kernel instance the Llama step runs too
+# (from bench.py --workload <name> --no-extra-decode --no-prefill), and the
+# Gemma-4 prefill layers (from a run with the extra prefill records, which the
+# main counter runs leave out: its mixed launch runs the Qwen3 fused-q
+# instance).
 PMC_SOLO_PARTS = {
     # one GPU's share of the Llama step at 8-way tensor parallelism: a
     # head_dim-128 key split like the Llama and Qwen3 calls
     "decode_llama_decode_tp8_share": (("decode_keysplit_kernel<128, ",), DECODE_SRC),
+    # the Gemma-4 prefill layers of extra_prefill (head_dim 256 and 512, the q
+    # transform loading its rotary rows: q mode 1), from a run with the extra
+    # prefill records, whose mixed launch shares the Qwen3 fused-q instance
+    # (the main counter and trace runs leave extra_prefill out)
+    "prefill_gemma_prefill_d256": (("prefill_kernel<256, ", ", 1>"), PREFILL_SRC),
+    "prefill_gemma_prefill_d512": (("prefill_kernel<512, ", ", 1>"), PREFILL_SRC),
 }
 
 
