@@ -380,22 +380,31 @@ def test_full_gemma_full_layer_all_rows():
     _full_check(case, hint)
 
 
-def test_decode_graph_replays_track_new_inputs():
+@pytest.mark.parametrize("shape", ["small", "large_grid"])
+def test_decode_graph_replays_track_new_inputs(shape):
     """One decode call (fused append) captured in a HIP graph and replayed with
     new q, new-token K/V and shorter lengths written into its static inputs
     between replays: every replay equals the eager call on the same inputs
-    bit for bit and matches the oracle.  (Replays reuse the library's split
-    arrival counters and the workspace; the path records no memset nodes.)"""
-    case = make_decode_case(32, 8, 128, 128, [900, 300, 0, 2049, 77], max_slots=7, seed=1700,
-                            spare_pages=2)
+    bit for bit and matches the oracle.  (Replays reuse the workspace's split
+    arrival counters; the path records no memset nodes.)  large_grid: the
+    64-row head_split shape, whose plan takes the short split 0, the late V
+    store and the early merge of split 0."""
+    if shape == "small":
+        case = make_decode_case(32, 8, 128, 128, [900, 300, 0, 2049, 77], max_slots=7,
+                                seed=1700, spare_pages=2)
+    else:
+        n_q, n_kv, D, ps, lengths, window, scale = CASES["head_split"]
+        case = make_decode_case(n_q, n_kv, D, ps, lengths, max_slots=len(lengths) + 2,
+                                seed=1710, spare_pages=2)
     kp, vp, table = gpu_decode_setup(case, with_new_token=False)
-    hint = 2049
-    ws = pkv.new_decode_workspace(pkv.decode_workspace_size(case.B, 32, 8, 128, hint), "cuda")
+    hint = int(case.seq_lens.max())
+    ws = pkv.new_decode_workspace(
+        pkv.decode_workspace_size(case.B, case.n_q, case.n_kv, case.head_dim, hint), "cuda")
     q_s = dev_bits(case.q)
     kn_s, vn_s = dev_bits(case.k_new), dev_bits(case.v_new)
     slots_s, lens_s = dev_i32(case.slots), dev_i32(case.seq_lens)
     out_s = torch.empty_like(q_s)
-    lse_s = torch.empty((case.B, 32), dtype=torch.float32, device=DEV)
+    lse_s = torch.empty((case.B, case.n_q), dtype=torch.float32, device=DEV)
 
     def call(out, lse):
         pkv.attn_decode(q_s, slots_s, lens_s, table, kp, vp, scale=case.scale,
