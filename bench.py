@@ -659,10 +659,11 @@ PMC_PARTS = {
     # part: (substrings a counted kernel instance's name contains, sources whose
     # hash the record keeps).  The three decode workloads run distinct
     # instances (Llama: 4-wave key split whose split 0 writes the new V;
-    # Qwen3: 8-wave key split; Gemma: the head_dim-256 and -512 dim-split
+    # Qwen3: the plain 4-wave key split (the main counter runs leave the
+    # tensor-parallel share, which runs it too, out); Gemma: the head_dim-256 and -512 dim-split
     # kernels, one call of each per step).
     "decode_llama_decode": (("decode_keysplit_kernel<128, 4, true>",), DECODE_SRC),
-    "decode_qwen3_decode": (("decode_keysplit_kernel<128, 8, ",), DECODE_SRC),
+    "decode_qwen3_decode": (("decode_keysplit_kernel<128, 4, false>",), DECODE_SRC),
     "decode_gemma_mixed": (("decode_dimsplit_kernel<",), DECODE_SRC),
     # prefill attention without the q transform (keys appended beforehand):
     # the instance of q mode 0

@@ -311,7 +311,6 @@ pkv_status attn_decode_impl(const char* fn, const void* q, int32_t n_q_heads,
   a.v_late = plan.v_late;
   a.early_merge = plan.early_merge;
   a.max_splits = plan.max_splits;
-  a.waves = plan.waves;
   a.part_o = plan.ws_bytes ? static_cast<uint32_t*>(workspace) : nullptr;
   a.part_ml = plan.ws_bytes ? reinterpret_cast<float*>(a.part_o + plan.part_o_words) : nullptr;
   // the counters sit at the end of the workspace as given, so every call that

@@ -512,8 +512,8 @@ __device__ __forceinline__ void idle_output(const DecodeArgs& a, int b, int hk, 
 }
 
 // ---------------------------------------------------------------------------
-// head_dim <= 128: key split across the NW waves of the workgroup (4, or 8
-// on short splits, see plan_decode); K rows through the waves' LDS stages.
+// head_dim <= 128: key split across the NW = 4 waves of the workgroup; K
+// rows through the waves' LDS stages.
 template <int D, int NW, bool VL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void decode_keysplit_kernel(const int32_t* slots, const int32_t* seq_lens, const int32_t* table,
@@ -902,7 +902,8 @@ void decode_dimsplit_kernel(const int32_t* slots, const int32_t* seq_lens, const
 }
 
 // Dynamic LDS of the key-split kernel: the larger of the waves' K stages and
-// their fp32 outputs (at most 64 KB: 8 waves * 32 keys * 128 * 2 bytes).
+// their fp32 outputs (at most 32 KB: 4 waves * 32 keys * 128 * 2 bytes, or
+// 4 waves * G * D * 4 bytes with G * D <= 2048).
 template <int D>
 size_t keysplit_lds_bytes(int waves, int G) {
   const size_t stage = (size_t)waves * 32 * D * 2, outs = (size_t)waves * G * D * sizeof(float);
@@ -918,11 +919,7 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t st) {
   // Qwen3).  Heads vary fastest, one per XCD when n_kv is 8.
   dim3 grid(a.g.n_kv, a.B, a.max_splits);
   if constexpr (D <= 128) {
-    if (a.waves == 8)
-      hipLaunchKernelGGL((decode_keysplit_kernel<D, 8, false>), grid, dim3(8 * 64),
-                         keysplit_lds_bytes<D>(8, a.G), st, a.slots, a.seq_lens, a.pt.table,
-                         a.max_splits, a);
-    else if (a.v_late)
+    if (a.v_late)
       hipLaunchKernelGGL((decode_keysplit_kernel<D, kDecodeWaves, true>), grid, dim3(kThreads),
                          keysplit_lds_bytes<D>(kDecodeWaves, a.G), st, a.slots, a.seq_lens,
                          a.pt.table, a.max_splits, a);
@@ -966,24 +963,18 @@ DecodePlan plan_decode(int B, int n_q, int n_kv, int head_dim, int max_seq_len_h
   // CU -- fewer workgroups than the budget above allows, so fewer set-ups and
   // partials to merge.  Measured on one GPU's share of the Llama shape under
   // 8-way tensor parallelism (64 rows, 3 query / 1 kv head): 21.5 us, against
-  // 24.1 / 26.7 / 40.6 with 256- / 1024- / 2048-key splits and 34.4 with the
-  // 8-wave short splits below; the full Llama shape already plans 512.
+  // 24.1 / 26.7 / 40.6 with 256- / 1024- / 2048-key splits and 34.4 with
+  // 8-wave workgroups over 256-key splits; the full Llama shape already
+  // plans 512.  (Short splits, one 32-key chunk per wave, once ran faster as
+  // 8-wave workgroups over 256 keys -- half the workgroups and partials; with
+  // the partials in bf16 the 4-wave 128-key splits win: Qwen3 call 11.05 ->
+  // 10.65 us.)
   if (head_dim <= 128 && split < 512 && pairs * ((range + 511) / 512) >= 256) split = 512;
-  // Short splits: when every wave of a 4-wave workgroup would get a single
-  // 32-key chunk, 8-wave workgroups over 256-key splits (half the workgroups,
-  // half the partials to merge) measured faster: Qwen3 shape 10.9 -> 10.2 us.
-  // Longer splits keep 4 waves (Llama shape: 97 us, against 112 with 8).
-  int waves = kDecodeWaves;
-  if (head_dim <= 128 && split == 32 * kDecodeWaves) {
-    waves = 8;
-    split = 32 * 8;
-  }
   p.split_tokens = (int)split;
   p.head_tokens = (int)split;
   p.v_late = 0;
   p.early_merge = 0;
   p.max_splits = (int)((range + split - 1) / split);
-  p.waves = waves;
   // A short split 0 on large full-causal grids: split 0 of every row is the
   // last layer of the grid to be dispatched, and the call ends as those
   // workgroups drain.  A quarter-length split 0 shortens that drain for one

@@ -72,7 +72,6 @@ struct DecodeArgs {
   int split_tokens;      // keys per split (multiple of 128)
   int head_tokens;       // keys of split 0 on full-causal rows (<= split_tokens)
   int max_splits;        // grid extent; 1 = no workspace, write out directly
-  int waves;             // wave64s per workgroup of the split kernel (4 or 8)
   uint32_t* part_o;      // [B][n_kv][max_splits][G][D/2] bf16 pairs of the split's o / l
   float* part_ml;        // [B][n_kv][max_splits][G][2]  (running max in log2 units, sum)
   uint32_t* arrivals_end;  // one past the split arrival counters: pair b*n_kv+hk at
@@ -181,7 +180,6 @@ struct DecodePlan {
   int v_late;
   int early_merge;
   int max_splits;
-  int waves;
   size_t ws_bytes;
   size_t part_o_words;   // partial outputs first (bf16 pairs), then the fp32 (max, sum) pairs
 };

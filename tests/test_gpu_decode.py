@@ -77,9 +77,9 @@ def test_decode_matches_oracle(name):
 
 # A length hint far above the real lengths makes the splits long (several
 # 32-key chunks per wave of 4-wave workgroups); the default hint of these
-# small cases gives 256-key splits over 8-wave workgroups (one chunk per
-# wave).  With 100000 the splits are 256 to 2048 keys, so the longer rows
-# still have several splits to merge.
+# small cases gives 128-key splits (one chunk per wave).  With 100000 the
+# splits are 256 to 2048 keys, so the longer rows still have several splits
+# to merge.
 LONG_SPLIT_HINT = 1_000_000
 
 
