@@ -235,6 +235,17 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t n_q_heads, int32_t n_kv_head
                                  int32_t head_dim, int32_t max_seq_len_hint,
                                  int32_t window);
 
+/* The split-K plan pkv_attn_decode makes for these sizes (host only, for
+ * inspection and tests): out[0] keys per split, out[1] keys of split 0 on
+ * full-causal rows, out[2] grid splits per (row, kv head), out[3] 1 when
+ * split 0 writes the fused append's new V (large grids), out[4] 1 when split
+ * 0 merges at once if the other splits are in, out[5] workspace bytes.
+ * out: host int64[6].  PKV_ERR_INVALID_ARG for a NULL out or sizes the
+ * decode call would reject as invalid (B, heads <= 0, n_q_heads not a
+ * multiple of n_kv_heads). */
+pkv_status pkv_decode_plan(int32_t B, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                           int32_t max_seq_len_hint, int32_t window, int64_t* out);
+
 /* ---------------------------------------------------------------------------
  * pkv_attn_prefill -- packed varlen prefill, K/V read from the pages.
  * Sequence n owns packed tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 of slot

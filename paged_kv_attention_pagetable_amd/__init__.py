@@ -113,6 +113,14 @@ def decode_workspace_size(B, n_q, n_kv, head_dim, max_seq_len_hint, window=0):
                                                window))
 
 
+def decode_plan(B, n_q, n_kv, head_dim, max_seq_len_hint, window=0):
+    """The split-K plan of pkv_attn_decode for these sizes (host only)."""
+    out = (ctypes.c_int64 * 6)()
+    check(lib().pkv_decode_plan(B, n_q, n_kv, head_dim, max_seq_len_hint, window, out))
+    return dict(split_tokens=out[0], head_tokens=out[1], max_splits=out[2],
+                v_late=bool(out[3]), early_merge=bool(out[4]), ws_bytes=out[5])
+
+
 def attn_decode(q, slots, seq_lens, table, k_pool, v_pool, scale=None, window=0,
                 max_seq_len_hint=None, out=None, lse=None, workspace=None, k_new=None,
                 v_new=None, stream=None):

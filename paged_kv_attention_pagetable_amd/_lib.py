@@ -68,6 +68,7 @@ _SIGS = {
                                           c_void_p, c_void_p, c_void_p, c_void_p, c_float,
                                           c_int32, c_void_p, c_void_p, c_void_p]),
     "pkv_decode_workspace_size": (c_size_t, [c_int32] * 6),
+    "pkv_decode_plan": (c_int32, [c_int32] * 6 + [ctypes.POINTER(ctypes.c_int64)]),
     "pkv_attn_prefill": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int32,
                                    c_int32, c_int32, PageTableRef, ctypes.POINTER(CacheDesc),
                                    c_void_p, c_void_p, c_float, c_int32,

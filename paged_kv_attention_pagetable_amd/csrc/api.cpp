@@ -231,6 +231,24 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t n_q_heads, int32_t n_kv_head
       .ws_bytes;
 }
 
+pkv_status pkv_decode_plan(int32_t B, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                           int32_t max_seq_len_hint, int32_t window, int64_t* out) {
+  static const char* fn = "pkv_decode_plan";
+  if (!out) return fail(PKV_ERR_INVALID_ARG, "%s: out is NULL", fn);
+  if (B <= 0 || n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "%s: need B, heads > 0 and n_q_heads %% n_kv_heads == 0", fn);
+  if (max_seq_len_hint < 1) max_seq_len_hint = 1;
+  const pkv::DecodePlan p = pkv::plan_decode(B, n_q_heads, n_kv_heads, head_dim,
+                                             max_seq_len_hint, window > 0 ? window : 0);
+  out[0] = p.split_tokens;
+  out[1] = p.head_tokens;
+  out[2] = p.max_splits;
+  out[3] = p.v_late;
+  out[4] = p.early_merge;
+  out[5] = (int64_t)p.ws_bytes;
+  return PKV_OK;
+}
+
 }  // extern "C"
 
 namespace {
